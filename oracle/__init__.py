@@ -1,0 +1,14 @@
+"""fp64 CPU oracle of the fused per-state norm + FC step.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the package smoke check and
+by bench.py's cpu_baseline leg, never by the product path.  It shares no code
+with the HIP library or its binding.
+"""
+
+from .fuse64 import (NORM_LN, NORM_NONE, NORM_RMS, decode_bf16, fold_apply, fold_prepare, fuse,
+                     fuse_bits, normalize, round_bf16_rne, row_stats)
+
+__all__ = [
+    "NORM_NONE", "NORM_LN", "NORM_RMS", "decode_bf16", "row_stats", "normalize", "fuse", "fuse_bits",
+    "fold_prepare", "fold_apply", "round_bf16_rne",
+]

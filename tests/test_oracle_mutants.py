@@ -1,0 +1,111 @@
+"""Planted mistakes in the oracle must fail at least one pin (CPU only).
+
+Each mutant is a copy of the oracle's fusion with one plausible slip: a
+dropped term, a wrong sign or index, a wrong estimator, a swapped operand.
+None of these is imported by anything else; they exist to show the pins
+have teeth.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins as pins
+
+NONE, LN, RMS = 0, 1, 2
+
+
+def _make(norm_fn, order=(0, 1, 2), use_bias=True, fc=None):
+    def fuse(H, kind, eps, gam, bet, W, bias):
+        parts = []
+        for s in order:
+            g = None if gam is None else gam[s]
+            b = None if bet is None else bet[s]
+            parts.append(norm_fn(np.asarray(H[s], float), kind, eps, g, b))
+        X = np.concatenate(parts, axis=1)
+        Y = X @ W if fc is None else fc(X, W)
+        if use_bias and bias is not None:
+            Y = Y + bias
+        return Y
+    return fuse
+
+
+def _ln_family(var_fn=None, eps_outside=False, affine=True, beta=True, rms_mean=False, gamma_first=False):
+    def norm(X, kind, eps, g, b):
+        d = X.shape[1]
+        g = np.ones(d) if g is None else g
+        b = np.zeros(d) if b is None else b
+        if kind == NONE:
+            return X.copy()
+        if kind == LN or (kind == RMS and rms_mean):
+            mu = X.mean(1)
+            v = ((X - mu[:, None]) ** 2).mean(1) if var_fn is None else var_fn(X, mu)
+            r = 1 / (np.sqrt(v) + eps) if eps_outside else 1 / np.sqrt(v + eps)
+            if gamma_first:
+                return (X * g - mu[:, None]) * r[:, None] + (b if beta else 0)
+            out = (X - mu[:, None]) * r[:, None]
+            if affine:
+                out = out * g
+            if beta and kind == LN:
+                out = out + b
+            return out
+        ms = (X * X).mean(1)
+        r = 1 / (np.sqrt(ms) + eps) if eps_outside else 1 / np.sqrt(ms + eps)
+        out = X * r[:, None]
+        return out * g if affine else out
+    return norm
+
+
+MUTANTS = {
+    "variance_without_centering": _make(_ln_family(var_fn=lambda X, mu: (X * X).mean(1))),
+    "unbiased_variance": _make(_ln_family(var_fn=lambda X, mu: ((X - mu[:, None]) ** 2).sum(1) / (X.shape[1] - 1))),
+    "eps_outside_sqrt": _make(_ln_family(eps_outside=True)),
+    "gamma_dropped": _make(_ln_family(affine=False)),
+    "beta_dropped": _make(_ln_family(beta=False)),
+    "rms_subtracts_mean": _make(_ln_family(rms_mean=True)),
+    "gamma_before_centering": _make(_ln_family(gamma_first=True)),
+    "segments_low_high_swapped": _make(_ln_family(), order=(2, 1, 0)),
+    "bias_dropped": _make(_ln_family(), use_bias=False),
+    "fc_sign_flipped": _make(_ln_family(), fc=lambda X, W: -(X @ W)),
+    "fc_rows_reversed_within_segment": _make(
+        _ln_family(), fc=lambda X, W: X @ np.concatenate(
+            [W[s * W.shape[1]:(s + 1) * W.shape[1]][::-1] for s in range(3)])),
+}
+
+
+def _all_pins(fuse_fn):
+    rng = np.random.default_rng(1)
+    d, M = 24, 6
+    H = [rng.normal(0, sc, (M, d)) + rng.normal(0, 0.5, d) for sc in (1.0, 4.0, 16.0)]
+    gam = [rng.normal(1, 0.1, d) for _ in range(3)]
+    W = rng.normal(0, (3 * d) ** -0.5, (3 * d, d))
+    bias = rng.normal(0, 0.01, d)
+    return {
+        "hand": pins.check_hand_example(fuse_fn),
+        "moments": pins.check_moments(fuse_fn, H),
+        "scale": pins.check_scale_invariance(fuse_fn, H, gam, W, bias),
+        "scale_eps": pins.check_scale_invariance_eps(fuse_fn, H, gam, W, bias),
+        "brute": pins.check_brute_force(fuse_fn),
+        "torch": pins.check_torch_library(fuse_fn),
+        "none": pins.check_none_is_eagle3(fuse_fn),
+        "order": pins.check_segment_order(fuse_fn),
+        "rows": pins.check_row_independence(fuse_fn),
+    }
+
+
+def test_pins_pass_on_oracle():
+    res = _all_pins(oracle.fuse)
+    assert all(res.values()), res
+
+
+def test_reference_copy_of_oracle_passes():
+    """The unmutated family used to build mutants passes every pin, so a
+    mutant's failure is due to its one slip."""
+    res = _all_pins(_make(_ln_family()))
+    assert all(res.values()), res
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    res = _all_pins(MUTANTS[name])
+    assert not all(res.values()), f"mutant {name} passed every pin: {res}"
