@@ -1,0 +1,20 @@
+"""EAGLE-3.1 normalized multi-layer feature fusion on MI355X (gfx950).
+
+    out = [norm(h_low) | norm(h_mid) | norm(h_high)] @ W + bias
+
+with a per-state LayerNorm (gamma_s, beta_s) or RMSNorm (gamma_s), or no norm
+(EAGLE-3).  Every step runs in the HIP kernels of libeagle31.so; this package
+only marshals torch tensors (device memory and the current stream) into the
+C ABI declared in include/eagle31.h.
+"""
+
+from __future__ import annotations
+
+from ._capi import (NORM_LAYERNORM, NORM_NONE, NORM_RMSNORM, Eagle31Error, LIB_PATH, lib)
+from .ops import (fold_prepare, fuse, fuse_folded, fuse_ws, norm_kind, release, row_stats, workspace_init,
+                  workspace_size)
+
+__all__ = [
+    "NORM_NONE", "NORM_LAYERNORM", "NORM_RMSNORM", "Eagle31Error", "LIB_PATH", "lib", "fuse", "fuse_ws",
+    "fold_prepare", "fuse_folded", "row_stats", "workspace_size", "workspace_init", "release", "norm_kind",
+]

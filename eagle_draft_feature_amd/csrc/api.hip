@@ -1,0 +1,442 @@
+// C ABI of the fused per-state norm + FC (declared in include/eagle31.h).
+//
+// Every argument check runs on the host before the first HIP call; a failed
+// check enqueues nothing.  Dispatch: M <= 64 runs the single-launch decode
+// kernel on W in its stored layout (or on the folded W'^T); larger M runs the
+// row-statistics pass and the folded GEMM, preparing W'^T, u and c into the
+// workspace first when the caller passed the stored W.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "../../include/eagle31.h"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace {
+
+using namespace e31;
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return EAGLE31_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;
+};
+
+bool overlaps(const void* p, size_t bytes, const void* q, size_t qbytes) {
+    if (p == nullptr || q == nullptr || bytes == 0 || qbytes == 0) return false;
+    const uintptr_t a0 = (uintptr_t)p, a1 = a0 + bytes, b0 = (uintptr_t)q, b1 = b0 + qbytes;
+    return a0 < b1 && b0 < a1;
+}
+
+constexpr int64_t MAX_M = 16777216;
+constexpr int64_t MAX_D = 65536;
+
+int check_common(int64_t M, int64_t d, int norm_kind, float eps) {
+    if (M < 0 || M > MAX_M || d <= 0 || d > MAX_D || (d % 64) != 0) return EAGLE31_ERR_SHAPE;
+    if (norm_kind != EAGLE31_NORM_NONE && norm_kind != EAGLE31_NORM_LAYERNORM && norm_kind != EAGLE31_NORM_RMSNORM)
+        return EAGLE31_ERR_NORM_KIND;
+    if (!std::isfinite(eps) || eps < 0.f) return EAGLE31_ERR_EPS;
+    return EAGLE31_OK;
+}
+
+int check_params(int64_t d, int norm_kind, const void* const* gamma, const void* const* beta) {
+    if (norm_kind != EAGLE31_NORM_NONE && gamma != nullptr)
+        for (int s = 0; s < 3; ++s)
+            if (gamma[s] != nullptr && !aligned16(gamma[s])) return EAGLE31_ERR_ALIGN;
+    if (norm_kind == EAGLE31_NORM_LAYERNORM && beta != nullptr)
+        for (int s = 0; s < 3; ++s)
+            if (beta[s] != nullptr && !aligned16(beta[s])) return EAGLE31_ERR_ALIGN;
+    (void)d;
+    return EAGLE31_OK;
+}
+
+int check_io(int64_t M, int64_t d, const void* h0, const void* h1, const void* h2, const void* out) {
+    if (M == 0) return EAGLE31_OK;
+    if (h0 == nullptr || h1 == nullptr || h2 == nullptr || out == nullptr) return EAGLE31_ERR_NULL;
+    if (!aligned16(h0) || !aligned16(h1) || !aligned16(h2) || !aligned16(out)) return EAGLE31_ERR_ALIGN;
+    const size_t hb = (size_t)M * (size_t)d * 2;
+    if (overlaps(out, hb, h0, hb) || overlaps(out, hb, h1, hb) || overlaps(out, hb, h2, hb)) return EAGLE31_ERR_ALIAS;
+    return EAGLE31_OK;
+}
+
+// ------------------------------------------------------------- workspace
+struct WsLayout {
+    size_t counters = 0, counters_bytes = 0;
+    size_t stats = 0, part = 0, mu = 0, rstd = 0, wt = 0, u = 0, c = 0;
+    size_t total = 0;
+};
+
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+
+// The workspace starts with a fixed region of synchronisation counters that
+// every call leaves at zero, whatever path (and so whatever layout of the
+// rest) the previous call used.
+constexpr size_t COUNTER_REGION = 16384;  // 4096 counters
+constexpr int MAX_COUNTERS = (int)(COUNTER_REGION / sizeof(int));
+
+WsLayout layout_for(int64_t M, int64_t d, int norm, bool folded) {
+    WsLayout L;
+    if (M <= 0) return L;
+    L.counters = 0;
+    L.counters_bytes = COUNTER_REGION;
+    size_t off = COUNTER_REGION;
+    if (M <= DECODE_MAX_M) {
+        const DecodePlan p = plan_decode((int)M, (int)d, norm, folded);
+        L.stats = off;
+        off += up256(p.stats_bytes);
+        L.part = off;
+        off += up256(p.part_bytes);
+        L.total = off;
+        return L;
+    }
+    const PrefillPlan p = plan_prefill((int)M, (int)d);
+    L.part = off;
+    off += up256(p.part_bytes);
+    L.mu = off;
+    off += up256((size_t)3 * M * sizeof(float));
+    L.rstd = off;
+    off += up256((size_t)3 * M * sizeof(float));
+    if (!folded) {
+        L.wt = off;
+        off += up256((size_t)3 * d * d * 2);
+        L.u = off;
+        off += up256((size_t)3 * d * sizeof(float));
+        L.c = off;
+        off += up256((size_t)d * sizeof(float));
+    }
+    L.total = off;
+    return L;
+}
+
+// Library-owned workspace: one buffer per (device, stream), grown on demand.
+// Counters are zeroed on allocation; every call leaves them at zero.
+struct OwnedWs {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+
+std::mutex g_ws_mutex;
+std::map<std::pair<int, void*>, OwnedWs> g_ws;
+
+int owned_workspace(size_t need, hipStream_t st, void** out_ptr, size_t* out_bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    OwnedWs& w = g_ws[std::make_pair(dev, (void*)st)];
+    if (w.bytes < need) {
+        if (w.ptr != nullptr) {
+            // work queued earlier may still use the old buffer
+            e = hipStreamSynchronize(st);
+            if (e != hipSuccess) return hip_fail(e);
+            e = hipFree(w.ptr);
+            if (e != hipSuccess) return hip_fail(e);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        size_t grow = need + need / 4;
+        grow = up256(grow);
+        e = hipMalloc(&w.ptr, grow);
+        if (e != hipSuccess) {
+            w.ptr = nullptr;
+            return hip_fail(e);
+        }
+        w.bytes = grow;
+        e = launch_zero(w.ptr, COUNTER_REGION, st);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    *out_ptr = w.ptr;
+    *out_bytes = w.bytes;
+    return EAGLE31_OK;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+    return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
+}
+
+// ------------------------------------------------------------- dispatch
+int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t d, int norm, float eps,
+             const void* const* gamma, const void* const* beta, const void* W, const void* bias, const void* wt,
+             const float* u, const float* c, bool folded, void* out, void* ws, size_t ws_bytes, hipStream_t st) {
+    const WsLayout L = layout_for(M, d, norm, folded);
+    if (ws_bytes < L.total) return EAGLE31_ERR_WORKSPACE;
+    const uint16_t* h[3] = {static_cast<const uint16_t*>(h0), static_cast<const uint16_t*>(h1),
+                            static_cast<const uint16_t*>(h2)};
+    const uint16_t* g[3] = {nullptr, nullptr, nullptr};
+    const uint16_t* b[3] = {nullptr, nullptr, nullptr};
+    if (!folded && norm != NORM_NONE && gamma != nullptr)
+        for (int s = 0; s < 3; ++s) g[s] = static_cast<const uint16_t*>(gamma[s]);
+    if (!folded && norm == NORM_LN && beta != nullptr)
+        for (int s = 0; s < 3; ++s) b[s] = static_cast<const uint16_t*>(beta[s]);
+
+    hipError_t e;
+    if (M <= DECODE_MAX_M) {
+        const DecodePlan p = plan_decode((int)M, (int)d, norm, folded);
+        if (p.nb > MAX_COUNTERS) return EAGLE31_ERR_SHAPE;
+        DecodeArgs a;
+        for (int s = 0; s < 3; ++s) {
+            a.h[s] = h[s];
+            a.gamma[s] = g[s];
+            a.beta[s] = b[s];
+        }
+        a.W = static_cast<const uint16_t*>(W);
+        a.wt = static_cast<const uint16_t*>(wt);
+        a.u = u;
+        a.c = c;
+        a.bias = folded ? nullptr : static_cast<const uint16_t*>(bias);
+        a.out = static_cast<uint16_t*>(out);
+        a.M = (int)M;
+        a.d = (int)d;
+        a.eps = eps;
+        a.nb = p.nb;
+        a.kps = p.kps;
+        a.counters = at<int>(ws, L.counters);
+        a.stats = at<float>(ws, L.stats);
+        a.part = at<float>(ws, L.part);
+        e = launch_decode(a, norm, folded, p, st);
+        if (e != hipSuccess) return hip_fail(e);
+        return EAGLE31_OK;
+    }
+
+    // prefill: statistics, (fold the stored W), GEMM
+    const PrefillPlan p = plan_prefill((int)M, (int)d);
+    if (p.splits > 1 && p.tiles_m * p.tiles_n > MAX_COUNTERS) return EAGLE31_ERR_SHAPE;
+    float* mu = at<float>(ws, L.mu);
+    float* rstd = at<float>(ws, L.rstd);
+    if (norm != NORM_NONE) {
+        e = launch_row_stats(h[0], h[1], h[2], (int)M, (int)d, norm, eps, mu, rstd, st);
+        if (e != hipSuccess) return hip_fail(e);
+    }
+    if (!folded) {
+        uint16_t* wtw = at<uint16_t>(ws, L.wt);
+        float* uw = at<float>(ws, L.u);
+        float* cw = at<float>(ws, L.c);
+        e = launch_fold_prepare((int)d, norm, g, b, static_cast<const uint16_t*>(W), static_cast<const uint16_t*>(bias),
+                                wtw, uw, cw, st);
+        if (e != hipSuccess) return hip_fail(e);
+        wt = wtw;
+        u = uw;
+        c = cw;
+    }
+    PrefillArgs a;
+    for (int s = 0; s < 3; ++s) a.h[s] = h[s];
+    a.wt = static_cast<const uint16_t*>(wt);
+    a.u = u;
+    a.c = c;
+    a.mu = mu;
+    a.rstd = rstd;
+    a.out = static_cast<uint16_t*>(out);
+    a.M = (int)M;
+    a.d = (int)d;
+    a.norm = norm;
+    a.splits = p.splits;
+    a.counters = at<int>(ws, L.counters);
+    a.part = at<float>(ws, L.part);
+    e = launch_prefill(a, p, st);
+    if (e != hipSuccess) return hip_fail(e);
+    return EAGLE31_OK;
+}
+
+int validate_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t d, int norm, float eps,
+                  const void* const* gamma, const void* const* beta, const void* W, const void* bias, void* out) {
+    int r = check_common(M, d, norm, eps);
+    if (r != EAGLE31_OK) return r;
+    if (W == nullptr) return EAGLE31_ERR_NULL;
+    if (!aligned16(W) || (bias != nullptr && !aligned16(bias))) return EAGLE31_ERR_ALIGN;
+    r = check_params(d, norm, gamma, beta);
+    if (r != EAGLE31_OK) return r;
+    r = check_io(M, d, h0, h1, h2, out);
+    if (r != EAGLE31_OK) return r;
+    if (M > 0) {
+        const size_t ob = (size_t)M * (size_t)d * 2;
+        if (overlaps(out, ob, W, (size_t)3 * d * d * 2) || overlaps(out, ob, bias, (size_t)d * 2)) return EAGLE31_ERR_ALIAS;
+        for (int s = 0; s < 3; ++s) {
+            if (gamma != nullptr && overlaps(out, ob, gamma[s], (size_t)d * 2)) return EAGLE31_ERR_ALIAS;
+            if (beta != nullptr && overlaps(out, ob, beta[s], (size_t)d * 2)) return EAGLE31_ERR_ALIAS;
+        }
+    }
+    return EAGLE31_OK;
+}
+
+int validate_folded(const void* h0, const void* h1, const void* h2, int64_t M, int64_t d, int norm, float eps,
+                    const void* wt, const float* u, const float* c, void* out) {
+    int r = check_common(M, d, norm, eps);
+    if (r != EAGLE31_OK) return r;
+    if (wt == nullptr || u == nullptr || c == nullptr) return EAGLE31_ERR_NULL;
+    if (!aligned16(wt) || !aligned16(u) || !aligned16(c)) return EAGLE31_ERR_ALIGN;
+    r = check_io(M, d, h0, h1, h2, out);
+    if (r != EAGLE31_OK) return r;
+    if (M > 0) {
+        const size_t ob = (size_t)M * (size_t)d * 2;
+        if (overlaps(out, ob, wt, (size_t)3 * d * d * 2) || overlaps(out, ob, u, (size_t)3 * d * 4) ||
+            overlaps(out, ob, c, (size_t)d * 4))
+            return EAGLE31_ERR_ALIAS;
+    }
+    return EAGLE31_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int eagle31_fuse(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d, int norm_kind,
+                 float eps, const void* const* gamma, const void* const* beta, const void* W, const void* bias,
+                 void* out, void* stream) {
+    int r = validate_fuse(h_low, h_mid, h_high, M, d, norm_kind, eps, gamma, beta, W, bias, out);
+    if (r != EAGLE31_OK || M == 0) return r;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    void* ws = nullptr;
+    size_t wsb = 0;
+    r = owned_workspace(layout_for(M, d, norm_kind, false).total, st, &ws, &wsb);
+    if (r != EAGLE31_OK) return r;
+    return run_fuse(h_low, h_mid, h_high, M, d, norm_kind, eps, gamma, beta, W, bias, nullptr, nullptr, nullptr,
+                    false, out, ws, wsb, st);
+}
+
+size_t eagle31_workspace_size(int64_t M, int64_t d, int norm_kind) {
+    if (check_common(M, d, norm_kind, 0.f) != EAGLE31_OK) return 0;
+    const WsLayout a = layout_for(M, d, norm_kind, false);
+    const WsLayout b = layout_for(M, d, norm_kind, true);
+    return a.total > b.total ? a.total : b.total;
+}
+
+int eagle31_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
+    if (workspace == nullptr) return EAGLE31_ERR_NULL;
+    if (((uintptr_t)workspace & 255u) != 0) return EAGLE31_ERR_ALIGN;
+    if (ws_bytes < COUNTER_REGION) return EAGLE31_ERR_WORKSPACE;
+    const hipError_t e = launch_zero(workspace, COUNTER_REGION, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return EAGLE31_OK;
+}
+
+int eagle31_fuse_ws(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d, int norm_kind,
+                    float eps, const void* const* gamma, const void* const* beta, const void* W, const void* bias,
+                    void* out, void* workspace, size_t ws_bytes, void* stream) {
+    int r = validate_fuse(h_low, h_mid, h_high, M, d, norm_kind, eps, gamma, beta, W, bias, out);
+    if (r != EAGLE31_OK || M == 0) return r;
+    if (workspace == nullptr) return EAGLE31_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return EAGLE31_ERR_ALIGN;
+    if (ws_bytes < layout_for(M, d, norm_kind, false).total) return EAGLE31_ERR_WORKSPACE;
+    return run_fuse(h_low, h_mid, h_high, M, d, norm_kind, eps, gamma, beta, W, bias, nullptr, nullptr, nullptr,
+                    false, out, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int eagle31_fold_prepare(int64_t d, int norm_kind, const void* const* gamma, const void* const* beta, const void* W,
+                         const void* bias, void* w_folded, float* u, float* c, void* stream) {
+    int r = check_common(0, d, norm_kind, 0.f);
+    if (r != EAGLE31_OK) return r;
+    if (W == nullptr || w_folded == nullptr || u == nullptr || c == nullptr) return EAGLE31_ERR_NULL;
+    if (!aligned16(W) || !aligned16(w_folded) || !aligned16(u) || !aligned16(c) ||
+        (bias != nullptr && !aligned16(bias)))
+        return EAGLE31_ERR_ALIGN;
+    r = check_params(d, norm_kind, gamma, beta);
+    if (r != EAGLE31_OK) return r;
+    const size_t wb = (size_t)3 * d * d * 2;
+    if (overlaps(w_folded, wb, W, wb) || overlaps(u, (size_t)3 * d * 4, W, wb) || overlaps(c, (size_t)d * 4, W, wb) ||
+        overlaps(u, (size_t)3 * d * 4, w_folded, wb) || overlaps(c, (size_t)d * 4, w_folded, wb) ||
+        overlaps(c, (size_t)d * 4, u, (size_t)3 * d * 4))
+        return EAGLE31_ERR_ALIAS;
+    const uint16_t* g[3] = {nullptr, nullptr, nullptr};
+    const uint16_t* b[3] = {nullptr, nullptr, nullptr};
+    if (norm_kind != NORM_NONE && gamma != nullptr)
+        for (int s = 0; s < 3; ++s) g[s] = static_cast<const uint16_t*>(gamma[s]);
+    if (norm_kind == NORM_LN && beta != nullptr)
+        for (int s = 0; s < 3; ++s) b[s] = static_cast<const uint16_t*>(beta[s]);
+    const hipError_t e = launch_fold_prepare((int)d, norm_kind, g, b, static_cast<const uint16_t*>(W),
+                                             static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(w_folded), u,
+                                             c, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return EAGLE31_OK;
+}
+
+int eagle31_fuse_folded(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d, int norm_kind,
+                        float eps, const void* w_folded, const float* u, const float* c, void* out, void* stream) {
+    int r = validate_folded(h_low, h_mid, h_high, M, d, norm_kind, eps, w_folded, u, c, out);
+    if (r != EAGLE31_OK || M == 0) return r;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    void* ws = nullptr;
+    size_t wsb = 0;
+    r = owned_workspace(layout_for(M, d, norm_kind, true).total, st, &ws, &wsb);
+    if (r != EAGLE31_OK) return r;
+    return run_fuse(h_low, h_mid, h_high, M, d, norm_kind, eps, nullptr, nullptr, nullptr, nullptr, w_folded, u, c,
+                    true, out, ws, wsb, st);
+}
+
+int eagle31_fuse_folded_ws(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d,
+                           int norm_kind, float eps, const void* w_folded, const float* u, const float* c, void* out,
+                           void* workspace, size_t ws_bytes, void* stream) {
+    int r = validate_folded(h_low, h_mid, h_high, M, d, norm_kind, eps, w_folded, u, c, out);
+    if (r != EAGLE31_OK || M == 0) return r;
+    if (workspace == nullptr) return EAGLE31_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return EAGLE31_ERR_ALIGN;
+    if (ws_bytes < layout_for(M, d, norm_kind, true).total) return EAGLE31_ERR_WORKSPACE;
+    return run_fuse(h_low, h_mid, h_high, M, d, norm_kind, eps, nullptr, nullptr, nullptr, nullptr, w_folded, u, c,
+                    true, out, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int eagle31_row_stats(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d, int norm_kind,
+                      float eps, float* mu, float* rstd, void* stream) {
+    int r = check_common(M, d, norm_kind, eps);
+    if (r != EAGLE31_OK || M == 0) return r;
+    if (h_low == nullptr || h_mid == nullptr || h_high == nullptr || mu == nullptr || rstd == nullptr)
+        return EAGLE31_ERR_NULL;
+    if (!aligned16(h_low) || !aligned16(h_mid) || !aligned16(h_high) || !aligned16(mu) || !aligned16(rstd))
+        return EAGLE31_ERR_ALIGN;
+    const hipError_t e = launch_row_stats(static_cast<const uint16_t*>(h_low), static_cast<const uint16_t*>(h_mid),
+                                          static_cast<const uint16_t*>(h_high), (int)M, (int)d, norm_kind, eps, mu,
+                                          rstd, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return EAGLE31_OK;
+}
+
+const char* eagle31_status_string(int status) {
+    switch (status) {
+        case EAGLE31_OK: return "ok";
+        case EAGLE31_ERR_NULL: return "a required pointer is NULL";
+        case EAGLE31_ERR_SHAPE: return "M or d out of range (d must be a positive multiple of 64)";
+        case EAGLE31_ERR_NORM_KIND: return "unknown norm_kind";
+        case EAGLE31_ERR_EPS: return "eps must be finite and >= 0";
+        case EAGLE31_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case EAGLE31_ERR_HIP: return "a HIP runtime call failed";
+        case EAGLE31_ERR_WORKSPACE: return "workspace missing or too small";
+        case EAGLE31_ERR_ALIAS: return "out overlaps an input";
+        default: return "unknown status";
+    }
+}
+
+int eagle31_last_hip_error(void) { return g_last_hip_error; }
+
+int eagle31_release(void) {
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e);
+    int rc = EAGLE31_OK;
+    for (auto& kv : g_ws) {
+        if (kv.second.ptr == nullptr) continue;
+        e = hipSetDevice(kv.first.first);
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e == hipSuccess) e = hipFree(kv.second.ptr);
+        if (e != hipSuccess) rc = hip_fail(e);
+        kv.second.ptr = nullptr;
+        kv.second.bytes = 0;
+    }
+    g_ws.clear();
+    (void)hipSetDevice(cur);
+    return rc;
+}
+
+}  // extern "C"

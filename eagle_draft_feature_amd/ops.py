@@ -1,0 +1,175 @@
+"""torch-facing wrappers of the C ABI: argument checks and pointer marshalling.
+
+torch provides device memory and the current HIP stream; nothing here
+computes.  All tensors must be contiguous bfloat16 (statistics and folded
+vectors float32) on the same GPU.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Sequence, Union
+
+import torch
+
+from . import _capi
+from ._capi import check, lib, ptr_array3
+
+_NAMES = {"none": _capi.NORM_NONE, "layernorm": _capi.NORM_LAYERNORM, "ln": _capi.NORM_LAYERNORM,
+          "rmsnorm": _capi.NORM_RMSNORM, "rms": _capi.NORM_RMSNORM}
+
+
+def norm_kind(kind: Union[int, str]) -> int:
+    if isinstance(kind, str):
+        return _NAMES[kind.lower()]
+    return int(kind)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _want(t: torch.Tensor, name: str, dtype=torch.bfloat16, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _vec3(ts: Optional[Sequence[Optional[torch.Tensor]]], name: str, d: int, device):
+    if ts is None:
+        return None
+    if len(ts) != 3:
+        raise ValueError(f"{name} needs three entries (low, mid, high)")
+    for i, t in enumerate(ts):
+        if t is not None:
+            _want(t, f"{name}[{i}]", shape=(d,), device=device)
+    return ptr_array3([_ptr(t) for t in ts])
+
+
+def _states(h_low, h_mid, h_high):
+    _want(h_low, "h_low")
+    if h_low.dim() != 2:
+        raise ValueError("hidden states must be [M, d]")
+    M, d = h_low.shape
+    for nm, t in (("h_mid", h_mid), ("h_high", h_high)):
+        _want(t, nm, shape=(M, d), device=h_low.device)
+    return M, d, h_low.device
+
+
+def fuse(h_low: torch.Tensor, h_mid: torch.Tensor, h_high: torch.Tensor, norm: Union[int, str], eps: float,
+         gammas: Optional[Sequence[Optional[torch.Tensor]]], betas: Optional[Sequence[Optional[torch.Tensor]]],
+         W: torch.Tensor, bias: Optional[torch.Tensor], out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[M, d] = [norm(h_low) | norm(h_mid) | norm(h_high)] @ W + bias (eagle31_fuse)."""
+    M, d, dev = _states(h_low, h_mid, h_high)
+    _want(W, "W", shape=(3 * d, d), device=dev)
+    if bias is not None:
+        _want(bias, "bias", shape=(d,), device=dev)
+    if out is None:
+        out = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    _want(out, "out", shape=(M, d), device=dev)
+    g = _vec3(gammas, "gammas", d, dev)
+    b = _vec3(betas, "betas", d, dev)
+    st = lib().eagle31_fuse(_ptr(h_low), _ptr(h_mid), _ptr(h_high), M, d, norm_kind(norm), float(eps),
+                            g[0] if g else None, b[0] if b else None, _ptr(W), _ptr(bias), _ptr(out),
+                            _stream(h_low))
+    check("eagle31_fuse", st)
+    return out
+
+
+def workspace_size(M: int, d: int, norm: Union[int, str]) -> int:
+    return int(lib().eagle31_workspace_size(M, d, norm_kind(norm)))
+
+
+def workspace_init(ws: torch.Tensor) -> None:
+    if not ws.is_cuda or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    check("eagle31_workspace_init", lib().eagle31_workspace_init(_ptr(ws), ws.numel() * ws.element_size(),
+                                                                  _stream(ws)))
+
+
+def fuse_ws(h_low, h_mid, h_high, norm, eps, gammas, betas, W, bias, workspace: torch.Tensor,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """eagle31_fuse_ws: as fuse(), with a caller workspace (see workspace_size / workspace_init)."""
+    M, d, dev = _states(h_low, h_mid, h_high)
+    _want(W, "W", shape=(3 * d, d), device=dev)
+    if bias is not None:
+        _want(bias, "bias", shape=(d,), device=dev)
+    if out is None:
+        out = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    _want(out, "out", shape=(M, d), device=dev)
+    g = _vec3(gammas, "gammas", d, dev)
+    b = _vec3(betas, "betas", d, dev)
+    st = lib().eagle31_fuse_ws(_ptr(h_low), _ptr(h_mid), _ptr(h_high), M, d, norm_kind(norm), float(eps),
+                               g[0] if g else None, b[0] if b else None, _ptr(W), _ptr(bias), _ptr(out),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(h_low))
+    check("eagle31_fuse_ws", st)
+    return out
+
+
+def fold_prepare(norm: Union[int, str], gammas, betas, W: torch.Tensor, bias: Optional[torch.Tensor]):
+    """eagle31_fold_prepare: returns (w_folded [d, 3d] bf16, u [3, d] f32, c [d] f32)."""
+    _want(W, "W")
+    if W.dim() != 2 or W.shape[0] != 3 * W.shape[1]:
+        raise ValueError("W must be [3d, d]")
+    d = W.shape[1]
+    dev = W.device
+    if bias is not None:
+        _want(bias, "bias", shape=(d,), device=dev)
+    wf = torch.empty((d, 3 * d), dtype=torch.bfloat16, device=dev)
+    u = torch.empty((3, d), dtype=torch.float32, device=dev)
+    c = torch.empty((d,), dtype=torch.float32, device=dev)
+    g = _vec3(gammas, "gammas", d, dev)
+    b = _vec3(betas, "betas", d, dev)
+    st = lib().eagle31_fold_prepare(d, norm_kind(norm), g[0] if g else None, b[0] if b else None, _ptr(W),
+                                    _ptr(bias), _ptr(wf), _ptr(u), _ptr(c), _stream(W))
+    check("eagle31_fold_prepare", st)
+    return wf, u, c
+
+
+def fuse_folded(h_low, h_mid, h_high, norm, eps, w_folded: torch.Tensor, u: torch.Tensor, c: torch.Tensor,
+                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """eagle31_fuse_folded (or _ws when a workspace is given) on prepared weights."""
+    M, d, dev = _states(h_low, h_mid, h_high)
+    _want(w_folded, "w_folded", shape=(d, 3 * d), device=dev)
+    _want(u, "u", dtype=torch.float32, shape=(3, d), device=dev)
+    _want(c, "c", dtype=torch.float32, shape=(d,), device=dev)
+    if out is None:
+        out = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    _want(out, "out", shape=(M, d), device=dev)
+    if workspace is None:
+        st = lib().eagle31_fuse_folded(_ptr(h_low), _ptr(h_mid), _ptr(h_high), M, d, norm_kind(norm), float(eps),
+                                       _ptr(w_folded), _ptr(u), _ptr(c), _ptr(out), _stream(h_low))
+        check("eagle31_fuse_folded", st)
+    else:
+        st = lib().eagle31_fuse_folded_ws(_ptr(h_low), _ptr(h_mid), _ptr(h_high), M, d, norm_kind(norm),
+                                          float(eps), _ptr(w_folded), _ptr(u), _ptr(c), _ptr(out), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream(h_low))
+        check("eagle31_fuse_folded_ws", st)
+    return out
+
+
+def row_stats(h_low, h_mid, h_high, norm, eps):
+    """eagle31_row_stats: returns (mu [3, M], rstd [3, M]) float32."""
+    M, d, dev = _states(h_low, h_mid, h_high)
+    mu = torch.empty((3, M), dtype=torch.float32, device=dev)
+    rstd = torch.empty((3, M), dtype=torch.float32, device=dev)
+    st = lib().eagle31_row_stats(_ptr(h_low), _ptr(h_mid), _ptr(h_high), M, d, norm_kind(norm), float(eps),
+                                 _ptr(mu), _ptr(rstd), _stream(h_low))
+    check("eagle31_row_stats", st)
+    return mu, rstd
+
+
+def release() -> None:
+    check("eagle31_release", lib().eagle31_release())

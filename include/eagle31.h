@@ -1,0 +1,175 @@
+/*
+ * eagle31.h - C ABI of the EAGLE-3.1 normalized multi-layer feature fusion
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (EAGLE 3.1 explainer, llm-wiki.hwlabs.dev/study/dist/ai-frontier/76.html,
+ * sections "EAGLE-3의 다층 특성 융합 구조" and "FC 정규화: EAGLE 3.1의 핵심 수정"):
+ * the target model's hidden states from an early, a middle and a late layer,
+ * h_low, h_mid, h_high (each [M, d], one row per token), are each normalised on
+ * their own, concatenated in that order to [M, 3d] and projected by the FC
+ * layer W [3d, d] (+ bias) to the draft head's input [M, d]:
+ *
+ *     out = [norm_0(h_low) | norm_1(h_mid) | norm_2(h_high)] . W + bias
+ *
+ * norm_s is one of (per state s, with its own gamma_s / beta_s):
+ *   EAGLE31_NORM_LAYERNORM  (x - mean) * (var + eps)^-1/2 * gamma_s + beta_s,
+ *                           var = mean((x - mean)^2) (divide by d);
+ *   EAGLE31_NORM_RMSNORM    x * (mean(x^2) + eps)^-1/2 * gamma_s   (the per-state
+ *                           RMSNorm of the vLLM EAGLE 3.1 release post,
+ *                           devlery.com/blog/vllm-eagle31-attention-drift, section
+ *                           "EAGLE 3.1이 바꾼 것은 작지만 낮은 계층입니다");
+ *   EAGLE31_NORM_NONE       identity: EAGLE-3's un-normalised fusion.
+ *
+ * Data types and layouts (all row-major, contiguous, no strides):
+ *   hidden states, gamma, beta, W, bias, out: bfloat16;
+ *   statistics and accumulation: float32; out is rounded to nearest even.
+ *   W is [3d, d]: element (k, n) at k*d + n; rows [s*d, (s+1)*d) multiply state s.
+ *
+ * Conventions shared by every entry point:
+ *   - pointers are device pointers on the calling thread's current HIP device,
+ *     16-byte aligned; the caller owns every buffer.  Work is enqueued on
+ *     `stream` (a hipStream_t passed as void*, NULL = default stream); the
+ *     caller keeps buffers alive until the stream has reached the work.
+ *   - arguments are checked on the host before any HIP call; a failed check
+ *     returns its status and enqueues nothing.  M == 0 returns EAGLE31_OK
+ *     without launching (h_* and out may then be NULL).
+ *   - limits: 1 <= d, d % 64 == 0, d <= 65536; 0 <= M <= 16777216;
+ *     eps finite and >= 0 (eps == 0 leaves constant rows undefined).
+ *   - out must not overlap any input.
+ *   - launch failures return EAGLE31_ERR_HIP (eagle31_last_hip_error() gives
+ *     the HIP code); faults inside kernels surface when the stream is
+ *     synchronised, as for any HIP work.  The library never prints or aborts.
+ *   - results are deterministic: the same inputs give the same bits.
+ */
+#ifndef EAGLE31_H
+#define EAGLE31_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum eagle31_norm_kind {
+    EAGLE31_NORM_NONE = 0,
+    EAGLE31_NORM_LAYERNORM = 1,
+    EAGLE31_NORM_RMSNORM = 2
+};
+
+enum eagle31_status {
+    EAGLE31_OK = 0,
+    EAGLE31_ERR_NULL = -1,       /* a required pointer is NULL */
+    EAGLE31_ERR_SHAPE = -2,      /* M or d out of range, d % 64 != 0 */
+    EAGLE31_ERR_NORM_KIND = -3,  /* norm_kind not one of eagle31_norm_kind */
+    EAGLE31_ERR_EPS = -4,        /* eps negative, NaN or infinite */
+    EAGLE31_ERR_ALIGN = -5,      /* a pointer is not 16-byte aligned */
+    EAGLE31_ERR_HIP = -6,        /* a HIP runtime call failed */
+    EAGLE31_ERR_WORKSPACE = -7,  /* caller workspace NULL or too small */
+    EAGLE31_ERR_ALIAS = -8       /* out overlaps an input */
+};
+
+/*
+ * eagle31_fuse - the fused step with library-owned scratch memory.
+ *
+ * gamma: array of 3 pointers (bf16 [d] each) or NULL; a NULL array or a NULL
+ *        entry means gamma_s = 1.  Ignored for EAGLE31_NORM_NONE.
+ * beta:  array of 3 pointers (bf16 [d] each) or NULL; NULL means beta_s = 0.
+ *        Used by EAGLE31_NORM_LAYERNORM only.
+ * bias:  bf16 [d] or NULL (no bias).
+ * out:   bf16 [M, d].
+ *
+ * Scratch memory (split-K partials, the folded weight of the large-M path,
+ * row statistics) is allocated by the library on first use per device and
+ * grown when a larger problem needs it; it is freed by eagle31_release().
+ * Allocation happens outside any kernel launch, so the first call at a new
+ * size may return EAGLE31_ERR_HIP if the device is out of memory.  Calls
+ * from several host threads are serialised on the scratch memory of a device.
+ */
+int eagle31_fuse(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d,
+                 int norm_kind, float eps, const void* const* gamma, const void* const* beta,
+                 const void* W, const void* bias, void* out, void* stream);
+
+/*
+ * eagle31_workspace_size - bytes of caller workspace eagle31_fuse_ws needs for
+ * (M, d, norm_kind).  Returns 0 for invalid arguments.
+ */
+size_t eagle31_workspace_size(int64_t M, int64_t d, int norm_kind);
+
+/*
+ * eagle31_workspace_init - zero the workspace's synchronisation counters.
+ * Must be enqueued once on a new workspace before its first eagle31_fuse_ws /
+ * eagle31_fuse_folded_ws call; every call leaves the counters at zero again.
+ */
+int eagle31_workspace_init(void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * eagle31_fuse_ws - eagle31_fuse with caller-provided workspace of at least
+ * eagle31_workspace_size(M, d, norm_kind) bytes (device memory, 256-byte
+ * aligned, initialised once with eagle31_workspace_init).  Calls that share a
+ * workspace must be ordered (same stream or synchronised).
+ */
+int eagle31_fuse_ws(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d,
+                    int norm_kind, float eps, const void* const* gamma, const void* const* beta,
+                    const void* W, const void* bias, void* out, void* workspace, size_t ws_bytes,
+                    void* stream);
+
+/*
+ * eagle31_fold_prepare - absorb the norm parameters into the FC once per
+ * weight set (EAGLE 3.1 explainer, section "FC 정규화: EAGLE 3.1의 핵심 수정":
+ * the LayerNorm parameters are taken into the FC layer, no weights are added).
+ *
+ * Outputs (caller-owned device memory):
+ *   w_folded  bf16 [d, 3d], the TRANSPOSED scaled weight: element (n, k) at
+ *             n*3d + k equals bf16_rne(gamma_s[k - s*d] * W[k, n]) for
+ *             LAYERNORM / RMSNORM and W[k, n] for NONE;
+ *   u         float32 [3, d]: u[s][n] = sum over k in state s of w_folded(n, k)
+ *             (from the stored, rounded values; zeros for NONE);
+ *   c         float32 [d]: c[n] = bias[n] + sum_s sum_k beta_s[k] W[s*d + k, n]
+ *             (the beta term for LAYERNORM only).
+ * Then, for the same norm_kind,
+ *   out = sum_s rstd_s * (h_s . w_folded_s^T - mu_s * u_s) + c
+ * equals eagle31_fuse's result up to rounding.
+ */
+int eagle31_fold_prepare(int64_t d, int norm_kind, const void* const* gamma, const void* const* beta,
+                         const void* W, const void* bias, void* w_folded, float* u, float* c,
+                         void* stream);
+
+/*
+ * eagle31_fuse_folded - the fused step on prepared weights (see
+ * eagle31_fold_prepare; norm_kind must be the one used to prepare them).
+ * Uses library-owned scratch memory like eagle31_fuse.
+ */
+int eagle31_fuse_folded(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d,
+                        int norm_kind, float eps, const void* w_folded, const float* u, const float* c,
+                        void* out, void* stream);
+
+/* eagle31_fuse_folded with caller workspace (same rules as eagle31_fuse_ws). */
+int eagle31_fuse_folded_ws(const void* h_low, const void* h_mid, const void* h_high, int64_t M,
+                           int64_t d, int norm_kind, float eps, const void* w_folded, const float* u,
+                           const float* c, void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * eagle31_row_stats - the statistics pass on its own: per state s and token m,
+ * mu[s*M + m] and rstd[s*M + m] (float32 [3, M]) as defined above
+ * (LAYERNORM: mean and (var + eps)^-1/2; RMSNORM: 0 and (mean(x^2) + eps)^-1/2;
+ * NONE: 0 and 1).
+ */
+int eagle31_row_stats(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d,
+                      int norm_kind, float eps, float* mu, float* rstd, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* eagle31_status_string(int status);
+
+/* HIP error code behind the calling thread's last EAGLE31_ERR_HIP (0 if none). */
+int eagle31_last_hip_error(void);
+
+/* Free the library-owned scratch memory of every device.  Not to be called
+ * while work that uses it is still queued. */
+int eagle31_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EAGLE31_H */

@@ -1,0 +1,140 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+symbol the header declares, and rejects bad arguments before any HIP call.
+
+Only argument validation and M == 0 are exercised here: every call below
+returns before the library touches the HIP runtime.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import eagle_draft_feature_amd as e31
+from eagle_draft_feature_amd import _capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "eagle31.h")
+
+# fake, 16-byte aligned device addresses: validation never dereferences them
+H0, H1, H2, WP, BP, OUT = 0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000
+
+
+def declared_symbols():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(eagle31_[a-z_]+)\s*\(", src)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = e31.lib()
+    syms = declared_symbols()
+    assert len(syms) >= 11
+    for s in syms:
+        assert hasattr(L, s), f"{s} declared in eagle31.h but not exported"
+    assert set(syms) == set(_capi.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def _fuse(**kw):
+    a = dict(h0=H0, h1=H1, h2=H2, M=4, d=128, norm=1, eps=1e-5, g=None, b=None, W=WP, bias=BP, out=OUT)
+    a.update(kw)
+    return e31.lib().eagle31_fuse(a["h0"], a["h1"], a["h2"], a["M"], a["d"], a["norm"], a["eps"], a["g"], a["b"],
+                                  a["W"], a["bias"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=100), _capi.ERR_SHAPE),
+    (dict(d=0), _capi.ERR_SHAPE),
+    (dict(d=-64), _capi.ERR_SHAPE),
+    (dict(d=65536 + 64), _capi.ERR_SHAPE),
+    (dict(M=-1), _capi.ERR_SHAPE),
+    (dict(M=16777217), _capi.ERR_SHAPE),
+    (dict(norm=3), _capi.ERR_NORM_KIND),
+    (dict(norm=-1), _capi.ERR_NORM_KIND),
+    (dict(eps=-1e-5), _capi.ERR_EPS),
+    (dict(eps=float("nan")), _capi.ERR_EPS),
+    (dict(eps=float("inf")), _capi.ERR_EPS),
+    (dict(h0=None), _capi.ERR_NULL),
+    (dict(h2=None), _capi.ERR_NULL),
+    (dict(out=None), _capi.ERR_NULL),
+    (dict(W=None), _capi.ERR_NULL),
+    (dict(h1=H1 + 2), _capi.ERR_ALIGN),
+    (dict(out=OUT + 8), _capi.ERR_ALIGN),
+    (dict(W=WP + 4), _capi.ERR_ALIGN),
+    (dict(bias=BP + 2), _capi.ERR_ALIGN),
+    (dict(out=H1 + 256), _capi.ERR_ALIAS),
+    (dict(out=WP + 1024), _capi.ERR_ALIAS),
+])
+def test_fuse_rejects_bad_arguments(kw, code):
+    assert _fuse(**kw) == code
+
+
+def test_fuse_M0_is_a_no_op():
+    assert _fuse(M=0, h0=None, h1=None, h2=None, out=None) == _capi.OK
+
+
+def test_fuse_gamma_beta_alignment_checked():
+    g, keep = _capi.ptr_array3([0x700000, 0x700102, 0x700200])
+    assert _fuse(g=g) == _capi.ERR_ALIGN
+    b, keep2 = _capi.ptr_array3([0x800000, None, 0x800208])
+    assert _fuse(b=b) == _capi.ERR_ALIGN
+    # beta is ignored for RMSNorm, gamma for NONE
+    assert _fuse(b=b, norm=2, M=0, h0=None, h1=None, h2=None, out=None) == _capi.OK
+    assert _fuse(g=g, norm=0, M=0, h0=None, h1=None, h2=None, out=None) == _capi.OK
+
+
+def test_folded_and_prepare_validation():
+    L = e31.lib()
+    f = L.eagle31_fuse_folded
+    assert f(H0, H1, H2, 4, 100, 1, 1e-5, WP, BP, 0x900000, OUT, None) == _capi.ERR_SHAPE
+    assert f(H0, H1, H2, 4, 128, 1, 1e-5, None, BP, 0x900000, OUT, None) == _capi.ERR_NULL
+    assert f(H0, H1, H2, 4, 128, 1, 1e-5, WP, BP + 4, 0x900000, OUT, None) == _capi.ERR_ALIGN
+    assert f(H0, H1, H2, 4, 128, 1, 1e-5, WP, BP, 0x900000, WP + 16, None) == _capi.ERR_ALIAS
+    assert f(None, None, None, 0, 128, 1, 1e-5, WP, BP, 0x900000, None, None) == _capi.OK
+    p = L.eagle31_fold_prepare
+    assert p(100, 1, None, None, WP, None, OUT, BP, 0x900000, None) == _capi.ERR_SHAPE
+    assert p(128, 1, None, None, None, None, OUT, BP, 0x900000, None) == _capi.ERR_NULL
+    assert p(128, 1, None, None, WP, None, WP + 64, BP, 0x900000, None) == _capi.ERR_ALIAS
+    assert p(128, 7, None, None, WP, None, OUT, BP, 0x900000, None) == _capi.ERR_NORM_KIND
+
+
+def test_workspace_entry_points_validation():
+    L = e31.lib()
+    assert L.eagle31_workspace_size(64, 4096, 1) > 0
+    assert L.eagle31_workspace_size(32768, 7168, 1) >= 3 * 7168 * 7168 * 2  # folded weight of the large-M path
+    assert L.eagle31_workspace_size(64, 100, 1) == 0
+    assert L.eagle31_workspace_init(None, 1024, None) == _capi.ERR_NULL
+    assert L.eagle31_workspace_init(0x100010, 1024, None) == _capi.ERR_ALIGN
+    fw = L.eagle31_fuse_ws
+    assert fw(H0, H1, H2, 4, 128, 1, 1e-5, None, None, WP, BP, OUT, None, 0, None) == _capi.ERR_WORKSPACE
+    assert fw(H0, H1, H2, 4, 128, 1, 1e-5, None, None, WP, BP, OUT, 0xA00000, 16, None) == _capi.ERR_WORKSPACE
+    assert fw(H0, H1, H2, 4, 128, 1, 1e-5, None, None, WP, BP, OUT, 0xA00010, 1 << 30, None) == _capi.ERR_ALIGN
+    assert fw(H0, H1, H2, 4, 100, 1, 1e-5, None, None, WP, BP, OUT, 0xA00000, 1 << 30, None) == _capi.ERR_SHAPE
+
+
+def test_row_stats_validation():
+    L = e31.lib()
+    r = L.eagle31_row_stats
+    assert r(H0, H1, H2, 4, 96, 1, 1e-5, OUT, BP, None) == _capi.ERR_SHAPE
+    assert r(H0, None, H2, 4, 128, 1, 1e-5, OUT, BP, None) == _capi.ERR_NULL
+    assert r(H0, H1, H2, 4, 128, 1, 1e-5, OUT + 4, BP, None) == _capi.ERR_ALIGN
+    assert r(None, None, None, 0, 128, 1, 1e-5, None, None, None) == _capi.OK
+
+
+def test_status_strings_and_last_hip_error():
+    L = e31.lib()
+    for code in _capi.STATUS_NAMES:
+        s = L.eagle31_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert L.eagle31_status_string(-99) == b"unknown status"
+    assert L.eagle31_last_hip_error() == 0
+
+
+def test_python_wrapper_checks_types_without_gpu():
+    import torch
+    x = torch.zeros(4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        e31.fuse(x, x, x, "ln", 1e-5, None, None, torch.zeros(384, 128, dtype=torch.bfloat16), None)
+    with pytest.raises(TypeError):
+        e31.fuse(x.float(), x, x, "ln", 1e-5, None, None, x, None)
