@@ -1,0 +1,350 @@
+"""Benchmark of the fused per-state norm + FC on one MI355X.
+
+One step = one eagle31_fuse call (every row of the hot path: statistics,
+normalisation, the FC contraction, epilogue) over one batch of synthetic
+tokens already resident in HBM.  Default workload: the 8B-shaped decode
+batch, d = 4096, M = 64 tokens (8 sequences x 8 draft tokens), LayerNorm
+with affine gamma/beta and an FC bias; W [12288, 4096] bf16 is 96 MiB.
+
+Cold cache: R copies of (W, hidden states, out) are rotated so the footprint
+is at least 512 MiB, twice the 256 MB MALL; every step reads a W that is not
+cache-resident, as a serving loop that streams many layers would.
+
+Prints ONE JSON line.  `value` is tokens/s over the K timed steps; the
+`roofline` object reports the decode kernel's algorithmic bytes per launch
+over its average launch duration (HIP events on the launch stream) against
+the 8 TB/s HBM peak; `cpu_baseline` times the fp64 oracle on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 * 1024 * 1024
+METRIC = "fused norm+FC tokens/s; % HBM peak (decode M) / % bf16 MFMA peak (prefill)"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--M", type=int, default=64, help="tokens of the headline decode step")
+    p.add_argument("--no-sweep", action="store_true", help="skip the per-M decode sweep")
+    p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurements")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
+    p.add_argument("--only", choices=["decode", "decode_folded", "prefill", "rowstats", "copy"], default=None,
+                   help="run a single leg (used under rocprofv3)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def alg_bytes(d, M, norm, has_beta, has_bias):
+    """W + three hidden states + out + bf16 parameter vectors, each once."""
+    nvec = 0
+    if norm == 1:
+        nvec = 3 + (3 if has_beta else 0)
+    elif norm == 2:
+        nvec = 3
+    return 3 * d * d * 2 + 3 * M * d * 2 + M * d * 2 + (nvec + (1 if has_bias else 0)) * d * 2
+
+
+def flops(d, M):
+    return 2 * M * 3 * d * d
+
+
+def to_dev(bits):
+    """bfloat16 bit patterns (numpy uint16) -> device tensor."""
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+class Rotation:
+    """R device copies of one problem instance (same values, distinct memory)."""
+
+    def __init__(self, inp, R, torch, with_W=True):
+        self.sets = []
+        base_h = [to_dev(x) for x in inp.h]
+        base_W = to_dev(inp.W) if with_W else None
+        for r in range(R):
+            h = [x.clone() for x in base_h] if r else base_h
+            W = (base_W.clone() if r else base_W) if with_W else None
+            out = torch.empty((inp.M, inp.d), dtype=torch.bfloat16, device="cuda")
+            self.sets.append((h, W, out))
+        self.gamma = [to_dev(x) for x in inp.gamma]
+        self.beta = None if inp.beta is None else [to_dev(x) for x in inp.beta]
+        self.bias = None if inp.bias is None else to_dev(inp.bias)
+
+
+def time_loop(torch, fn, R, steps, warmup, per_call_events=False):
+    for i in range(warmup):
+        fn(i % R)
+    torch.cuda.synchronize()
+    if per_call_events:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record()
+            fn(i % R)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        durs = [a.elapsed_time(b) * 1e3 for a, b in ev]  # microseconds
+        return durs
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        fn(i % R)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return t0.elapsed_time(t1) * 1e-3, wall
+
+
+_INPUTS = {}
+
+
+def cached_inputs(synth, cfg, M):
+    key = (cfg, M)
+    if key not in _INPUTS:
+        if len(_INPUTS) >= 2:
+            _INPUTS.clear()
+        _INPUTS[key] = synth.make_inputs(cfg, M)
+    return _INPUTS[key]
+
+
+def rotation_count(footprint):
+    return max(2, -(-2 * MALL_BYTES // footprint))
+
+
+def decode_leg(torch, pkg, synth, M, steps, warmup, repeats=5):
+    w = synth.CONFIGS[2]
+    inp = cached_inputs(synth, 2, 64).rows(M)
+    kind, eps = w.norms[0]
+    foot = 3 * inp.d * inp.d * 2 + 4 * M * inp.d * 2
+    R = rotation_count(foot)
+    rot = Rotation(inp, R, torch)
+
+    def fn(i):
+        h, W, out = rot.sets[i]
+        pkg.fuse(h[0], h[1], h[2], kind, eps, rot.gamma, rot.beta, W, rot.bias, out)
+
+    totals = []
+    for _ in range(repeats):
+        t, wall = time_loop(torch, fn, R, steps, warmup)
+        totals.append(t)
+    t_med = statistics.median(totals)
+    durs = time_loop(torch, fn, R, steps, warmup, per_call_events=True)
+    nbytes = alg_bytes(inp.d, M, kind, inp.beta is not None, inp.bias is not None)
+    return dict(M=M, d=inp.d, R=R, seconds=t_med, seconds_all=totals, steps=steps,
+                us_per_step=t_med / steps * 1e6, event_us_mean=statistics.mean(durs),
+                event_us_median=statistics.median(durs), bytes=nbytes, inp=inp, kind=kind, eps=eps)
+
+
+def folded_decode_leg(torch, pkg, synth, M, steps, warmup):
+    inp = cached_inputs(synth, 2, 64).rows(M)
+    kind, eps = synth.CONFIGS[2].norms[0]
+    foot = 3 * inp.d * inp.d * 2 + 4 * M * inp.d * 2
+    R = rotation_count(foot)
+    rot = Rotation(inp, R, torch)
+    folded = [pkg.fold_prepare(kind, rot.gamma, rot.beta, W, rot.bias) for (_, W, _) in rot.sets]
+
+    def fn(i):
+        h, _, out = rot.sets[i]
+        wf, u, c = folded[i]
+        pkg.fuse_folded(h[0], h[1], h[2], kind, eps, wf, u, c, out)
+
+    t, _ = time_loop(torch, fn, R, steps, warmup)
+    return dict(M=M, us_per_step=t / steps * 1e6, tokens_per_s=M * steps / t,
+                hbm_frac=alg_bytes(inp.d, M, 0, False, False) / (t / steps) / 1e9 / HBM_PEAK_GBS)
+
+
+def prefill_leg(torch, pkg, synth, cfg, M, kind, eps, steps, warmup, folded=False):
+    inp = cached_inputs(synth, cfg, M)
+    foot = 3 * inp.d * inp.d * 2 + 4 * M * inp.d * 2
+    R = 2 if foot >= MALL_BYTES else rotation_count(foot)
+    rot = Rotation(inp, R, torch)
+    if folded:
+        prepared = [pkg.fold_prepare(kind, rot.gamma, rot.beta, W, rot.bias) for (_, W, _) in rot.sets]
+
+    def fn(i):
+        h, W, out = rot.sets[i]
+        if folded:
+            wf, u, c = prepared[i]
+            pkg.fuse_folded(h[0], h[1], h[2], kind, eps, wf, u, c, out)
+        else:
+            pkg.fuse(h[0], h[1], h[2], kind, eps, rot.gamma, rot.beta, W, rot.bias, out)
+
+    t, _ = time_loop(torch, fn, R, steps, warmup)
+    per = t / steps
+    res = dict(workload=synth.CONFIGS[cfg].name, d=inp.d, M=M, norm=kind, variant="folded" if folded else "plain",
+               ms_per_step=per * 1e3, tokens_per_s=M / per,
+               mfma_frac=flops(inp.d, M) / per / 1e12 / BF16_PEAK_TFLOPS,
+               tflops=flops(inp.d, M) / per / 1e12)
+    del rot
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline_leg(inp, kind, eps, budget_s):
+    """The fp64 oracle as it stands, on preconverted float64 arrays, repeated
+    until about budget_s seconds of host work."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    H = [oracle.decode_bf16(h) for h in inp.h]
+    g = [oracle.decode_bf16(x) for x in inp.gamma]
+    b = None if inp.beta is None else [oracle.decode_bf16(x) for x in inp.beta]
+    W = oracle.decode_bf16(inp.W)
+    bias = None if inp.bias is None else oracle.decode_bf16(inp.bias)
+    oracle.fuse(H, kind, eps, g, b, W, bias)  # warm BLAS
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.fuse(H, kind, eps, g, b, W, bias)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 10000:
+            break
+    return dict(value=inp.M * n / el, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{n} oracle calls of the full decode batch (d={inp.d}, M={inp.M}) on float64 "
+                       f"arrays, {el:.1f} s; BLAS threads {threads}")
+
+
+def copy_leg(torch, nbytes=1 << 30, steps=20):
+    """A plain device copy of known size (counter calibration reference)."""
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    bb = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(3):
+        bb.copy_(a)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        bb.copy_(a)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    return dict(bytes_per_copy=nbytes, gbs=2 * nbytes * steps / el / 1e9)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the fused step is row independent and this build runs on a "
+              "single MI355X (multi-GPU sharding is a design note, not measured). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import eagle_draft_feature_amd as pkg
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pkg.lib()
+
+    if args.only == "copy":
+        print(json.dumps(copy_leg(torch)))
+        return
+    if args.only == "prefill":
+        print(json.dumps(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, max(3, args.steps), args.warmup)))
+        return
+    if args.only == "rowstats":
+        inp = synth.make_inputs(4, with_weights=False)
+        h = [to_dev(x) for x in inp.h]
+        for _ in range(args.warmup):
+            pkg.row_stats(h[0], h[1], h[2], 1, 1e-5)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            pkg.row_stats(h[0], h[1], h[2], 1, 1e-5)
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) / args.steps
+        print(json.dumps(dict(rowstats_us=el * 1e6, gbs=3 * inp.M * inp.d * 2 / el / 1e9)))
+        return
+
+    if args.only == "decode_folded":
+        f = folded_decode_leg(torch, pkg, synth, args.M, args.steps, args.warmup)
+        print(json.dumps(f))
+        return
+    dec = decode_leg(torch, pkg, synth, args.M, args.steps, args.warmup)
+    if args.only == "decode":
+        print(json.dumps({k: v for k, v in dec.items() if k != "inp"}))
+        return
+
+    value = args.M * dec["steps"] / dec["seconds"]
+    kern_us = dec["event_us_mean"]
+    achieved = dec["bytes"] / (kern_us * 1e-6) / 1e9
+    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="decode_kernel (eagle31_fuse, M<=64)",
+                    bytes_per_launch=dec["bytes"], launch_us_mean=round(kern_us, 3))
+
+    sweep = []
+    if not args.no_sweep:
+        for M in (1, 4, 8, 16, 64):
+            r = dec if M == args.M else decode_leg(torch, pkg, synth, M, args.steps, args.warmup, repeats=3)
+            per = r["seconds"] / r["steps"]
+            sweep.append(dict(M=M, us_per_step=round(per * 1e6, 3), tokens_per_s=round(M / per, 1),
+                              hbm_frac=round(r["bytes"] / per / 1e9 / HBM_PEAK_GBS, 4),
+                              event_us_mean=round(r["event_us_mean"], 3)))
+        for M in (1, 64):
+            f = folded_decode_leg(torch, pkg, synth, M, args.steps, args.warmup)
+            sweep.append(dict(M=M, variant="folded", us_per_step=round(f["us_per_step"], 3),
+                              tokens_per_s=round(f["tokens_per_s"], 1), hbm_frac=round(f["hbm_frac"], 4)))
+
+    prefill = []
+    if not args.no_prefill:
+        prefill.append(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, 10, 3, folded=False))
+        prefill.append(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, 10, 3, folded=True))
+        prefill.append(prefill_leg(torch, pkg, synth, 5, 4096, 1, 1e-5, 30, 5, folded=False))
+        prefill.append(prefill_leg(torch, pkg, synth, 5, 4096, 1, 1e-5, 30, 5, folded=True))
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline_leg(dec["inp"], dec["kind"], dec["eps"], args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["seconds"] / dec["steps"] * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode_ln_d4096", "d": dec["d"], "M": args.M, "norm": "layernorm",
+                   "eps": dec["eps"], "W": [3 * dec["d"], dec["d"]], "bias": True,
+                   "cold_cache_rotation": dec["R"], "entry_point": "eagle31_fuse"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "decode_sweep": sweep,
+        "prefill": prefill,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

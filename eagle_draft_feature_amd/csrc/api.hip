@@ -84,6 +84,9 @@ size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 // rest) the previous call used.
 constexpr size_t COUNTER_REGION = 16384;  // 4096 counters
 constexpr int MAX_COUNTERS = (int)(COUNTER_REGION / sizeof(int));
+// the folded weight's column-block kernel reads all tokens per column block:
+// it wins while the token fragments are few; beyond that the split-K kernel does
+constexpr int64_t DECODE_COLS_MAX_M = 16;
 
 WsLayout layout_for(int64_t M, int64_t d, int norm, bool folded) {
     WsLayout L;
@@ -91,6 +94,14 @@ WsLayout layout_for(int64_t M, int64_t d, int norm, bool folded) {
     L.counters = 0;
     L.counters_bytes = COUNTER_REGION;
     size_t off = COUNTER_REGION;
+    if (M <= DECODE_COLS_MAX_M && folded) {
+        L.mu = off;
+        off += up256((size_t)3 * M * sizeof(float));
+        L.rstd = off;
+        off += up256((size_t)3 * M * sizeof(float));
+        L.total = off;
+        return L;
+    }
     if (M <= DECODE_MAX_M) {
         const DecodePlan p = plan_decode((int)M, (int)d, norm, folded);
         L.stats = off;
@@ -181,6 +192,30 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
         for (int s = 0; s < 3; ++s) b[s] = static_cast<const uint16_t*>(beta[s]);
 
     hipError_t e;
+    if (M <= DECODE_COLS_MAX_M && folded) {
+        float* mu = at<float>(ws, L.mu);
+        float* rstd = at<float>(ws, L.rstd);
+        const bool instats = M <= 16;
+        if (norm != NORM_NONE && !instats) {
+            e = launch_row_stats(h[0], h[1], h[2], (int)M, (int)d, norm, eps, mu, rstd, st);
+            if (e != hipSuccess) return hip_fail(e);
+        }
+        DecodeColsArgs a;
+        a.eps = eps;
+        a.instats = instats;
+        for (int s = 0; s < 3; ++s) a.h[s] = h[s];
+        a.wt = static_cast<const uint16_t*>(wt);
+        a.u = u;
+        a.c = c;
+        a.mu = mu;
+        a.rstd = rstd;
+        a.out = static_cast<uint16_t*>(out);
+        a.M = (int)M;
+        a.d = (int)d;
+        e = launch_decode_cols(a, norm, st);
+        if (e != hipSuccess) return hip_fail(e);
+        return EAGLE31_OK;
+    }
     if (M <= DECODE_MAX_M) {
         const DecodePlan p = plan_decode((int)M, (int)d, norm, folded);
         if (p.nb > MAX_COUNTERS) return EAGLE31_ERR_SHAPE;

@@ -10,32 +10,38 @@
 // cores (a wave64 VALU GEMV at M = 64 would need more than the chip's FP32 rate).
 //
 // Design (one launch):
-//  * Work is split over (column block b of 16*J columns) x (K chunk c); a
-//    chunk never crosses a state boundary.  Workgroup (b, c) streams its
-//    [chunk, 16*J] slice of W exactly once, in the stored row-major layout.
-//    Each lane loads 8 consecutive rows x J consecutive columns and
-//    transposes that 8 x J block in registers into J MFMA B operands
-//    (8 consecutive k of one column each): half a byte-permute per element.
+//  * Work is split over (column block b of 16*J columns) x (K chunk c), one
+//    8-wave workgroup per pair and about one workgroup per CU.  Workgroup
+//    (b, c) streams its [chunk, 16*J] slice of W exactly once, in the stored
+//    row-major layout: each lane loads 8 consecutive rows x J consecutive
+//    columns and transposes that 8 x J block in registers into J MFMA B
+//    operands (8 consecutive k of one column each): half a byte-permute per
+//    element.  The folded variant streams W'^T instead, whose 16-byte rows
+//    are MFMA operands as loaded.
+//  * A chunk that crosses a state boundary is processed as pieces, one per
+//    state; every piece has its own partial tile and statistics.
 //  * The A operand is built on the fly from the raw hidden states: LayerNorm
 //    needs the row mean before rounding to bf16, which is not known inside a
-//    chunk, so the chunk subtracts a provisional shift K_c (mean of the
-//    chunk's first 32 values of that row) and multiplies by gamma:
-//        a = bf16((x - K_c) * gamma).
+//    piece, so the piece subtracts a provisional shift K_p (mean of the
+//    piece's first 32 values of that row) and multiplies by gamma:
+//        a = bf16((x - K_p) * gamma).
 //    Rows M and M+1 of the A operand carry gamma and beta themselves, so the
-//    same MFMAs also produce U_c = sum_k gamma_k W_kn and C_c = sum_k beta_k W_kn.
+//    same MFMAs also produce U_p = sum_k gamma_k W_kn and C_p = sum_k beta_k W_kn.
 //    In exact arithmetic, with mu and rstd the state's statistics,
-//        sum_k n(x)_k W_kn = rstd * sum_c (P_c - (mu - K_c) U_c) + sum_c C_c,
-//    where P_c = sum_{k in c} (x_k - K_c) gamma_k W_kn.  Subtracting a shift
+//        sum_k n(x)_k W_kn = rstd * sum_p (P_p - (mu - K_p) U_p) + sum_p C_p,
+//    where P_p = sum_{k in p} (x_k - K_p) gamma_k W_kn.  Subtracting a shift
 //    close to the mean before rounding keeps the bf16 rounding error relative
 //    to the row's spread, not to its offset.
-//  * The chunk statistics come from the same A fragments: shifted sums
-//    S1 = sum (x - K_c) and S2 = sum (x - K_c)^2 (RMSNorm: sum x^2), so no
+//  * The piece statistics come from the same A fragments: shifted sums
+//    S1 = sum (x - K_p) and S2 = sum (x - K_p)^2 (RMSNorm: sum x^2), so no
 //    extra pass over the hidden states is made.
-//  * Partials [rows, 16*J] and chunk statistics go to a workspace; the last
-//    workgroup of a column block to arrive (atomic counter) combines the
-//    statistics of all chunks (exact shifted-sum algebra in float64), forms
-//    mu and rstd, and sums the partials in a fixed chunk order: the result
-//    is bitwise reproducible.  It resets the counter for the next call.
+//  * The 8 waves of a workgroup sum their tiles pairwise in LDS in a fixed
+//    order; the workgroup writes a compact row-major partial and its piece
+//    statistics to the workspace.  The last workgroup of a column block to
+//    arrive (atomic counter) combines the statistics (exact shifted-sum
+//    algebra in float64), issues every partial load of its outputs at once,
+//    sums the pieces in a fixed order and resets the counter: the result is
+//    bitwise reproducible and the workspace is ready for the next call.
 #include <type_traits>
 
 #include "common.hpp"
@@ -43,9 +49,11 @@
 
 namespace e31 {
 
-constexpr int DW = 4;               // waves per workgroup
+constexpr int DW = 8;                           // waves per workgroup
 constexpr int DTHREADS = 64 * DW;
-constexpr int DECODE_MAX_KPS = 16;  // K chunks per state segment, at most
+constexpr int DECODE_MAX_KS = 8;                // K chunks per column block
+constexpr int DECODE_SLOTS = 3;                 // piece slots per chunk
+constexpr int PPS = 4;                          // pieces per state, at most (ks <= 8)
 
 template <int J>
 struct RowVec;
@@ -66,7 +74,6 @@ __device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
     return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-// rows of the A operand that are stored: tokens, then the gamma and beta rows (LayerNorm)
 // rows of the A operand after the tokens: gamma and beta (LayerNorm on the
 // stored W; the folded variant gets u and c from the prepare step instead)
 template <int NORM, bool FOLDED>
@@ -80,28 +87,29 @@ template <int NORM, int J, int MT, bool FOLDED>
 __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
     constexpr int NW = 16 * J;
     constexpr int ROWS = 16 * MT;
+    constexpr int FR = MT * J;            // f32x4 accumulators per lane
+    constexpr int TILE = ROWS * NW;       // floats of one wave tile
+    constexpr int RG = DTHREADS / NW;     // row groups of the reducer
+    constexpr int MAXROWS = ROWS < DECODE_MAX_M ? ROWS : DECODE_MAX_M;
+    constexpr int RPT = (MAXROWS + RG - 1) / RG;  // reducer rows per thread
     typedef typename RowVec<J>::T BT;
+    typedef typename std::conditional<FOLDED, uint4, BT>::type LT;
+    constexpr int NL = FOLDED ? J : 8;
 
-    const int nb = a.nb, kps = a.kps, M = a.M, d = a.d;
-    const int nchunks = 3 * kps;
+    const int nb = a.nb, ks = a.kps, M = a.M, d = a.d;
     const int b = blockIdx.x % nb;
     const int c = blockIdx.x / nb;
-    const int s = c / kps;
-    const int cj = c - s * kps;
     const int TS = d >> 5;
-    const int t0 = s * TS + (cj * TS) / kps;
-    const int t1 = s * TS + ((cj + 1) * TS) / kps;
+    const int T = 3 * TS;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, cb = lane & 15;
     const int n0 = b * NW;
-    const int seg_k0 = s * d;
-    const uint16_t* __restrict__ hs = a.h[s];
-    const uint16_t* __restrict__ gam = a.gamma[s];
-    const uint16_t* __restrict__ bet = a.beta[s];
+    const int Mst = M + param_rows<NORM, FOLDED>();
     const uint16_t* __restrict__ W = a.W;
 
-    // wave-combine buffers (2 x ROWS x NW floats), reused by the reducer for mu - K_c
-    constexpr int BIG = (2 * ROWS * NW > 3 * DECODE_MAX_KPS * DECODE_MAX_M) ? 2 * ROWS * NW
-                                                                             : 3 * DECODE_MAX_KPS * DECODE_MAX_M;
+    // big: 4 wave tiles for the pairwise sums; reused for the row-major tile
+    // and, in the reducer, for (mu - K_p) per piece
+    constexpr int BIG = 4 * TILE;
+    static_assert(BIG >= 3 * PPS * DECODE_MAX_M, "reducer scratch");
     __shared__ __attribute__((aligned(16))) float sh_big[BIG];
     __shared__ float sh_shift[DECODE_MAX_M];
     __shared__ float sh_s1[DW][DECODE_MAX_M];
@@ -110,339 +118,362 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
     __shared__ float sh_mu[3][DECODE_MAX_M];
     __shared__ int sh_last;
 
-    // ---- provisional shift per token row: mean of the chunk's first 32 values
-    if (NORM == NORM_LN) {
-        const int m = tid >> 2;
-        if (m < M) {
-            const uint4 x = *reinterpret_cast<const uint4*>(hs + (size_t)m * d + (t0 * 32 - seg_k0) + (tid & 3) * 8);
-            float v = bf_lo(x.x) + bf_hi(x.x) + bf_lo(x.y) + bf_hi(x.y) + bf_lo(x.z) + bf_hi(x.z) + bf_lo(x.w) +
-                      bf_hi(x.w);
-            v += __shfl_xor(v, 1, 64);
-            v += __shfl_xor(v, 2, 64);
-            if ((tid & 3) == 0) sh_shift[m] = v * (1.0f / 32.0f);
+    // chunk c covers k-steps [t0c, t1c); piece pi is its part in state s_first + pi
+    const int t0c = (c * T) / ks, t1c = ((c + 1) * T) / ks;
+    const int s_first = t0c / TS;
+    const int npieces = (t1c - 1) / TS - s_first + 1;
+
+    for (int pi = 0; pi < npieces; ++pi) {
+        const int s = s_first + pi;
+        const int tp0 = max(t0c, s * TS), tp1 = min(t1c, (s + 1) * TS);
+        const int seg_k0 = s * d;
+        const uint16_t* __restrict__ hs = a.h[s];
+        const uint16_t* __restrict__ gam = a.gamma[s];
+        const uint16_t* __restrict__ bet = a.beta[s];
+
+        // ---- provisional shift per token row: mean of the piece's first 32 values
+        if (NORM == NORM_LN && tid < 4 * DECODE_MAX_M) {
+            const int m = tid >> 2;
+            if (m < M) {
+                const uint4 x =
+                    *reinterpret_cast<const uint4*>(hs + (size_t)m * d + (tp0 * 32 - seg_k0) + (tid & 3) * 8);
+                float v = bf_lo(x.x) + bf_hi(x.x) + bf_lo(x.y) + bf_hi(x.y) + bf_lo(x.z) + bf_hi(x.z) +
+                          bf_lo(x.w) + bf_hi(x.w);
+                v += __shfl_xor(v, 1, 64);
+                v += __shfl_xor(v, 2, 64);
+                if ((tid & 3) == 0) sh_shift[m] = v * (1.0f / 32.0f);
+            }
         }
         __syncthreads();
-    }
 
-    // ---- per-lane role of each 16-row tile of the A operand
-    float shift[MT];
-    int role[MT];  // 0 token, 1 gamma row, 2 beta row, 3 zero
-#pragma unroll
-    for (int tt = 0; tt < MT; ++tt) {
-        const int m = 16 * tt + cb;
-        shift[tt] = 0.f;
-        if (m < M) {
-            role[tt] = 0;
-            if (NORM == NORM_LN) shift[tt] = sh_shift[m];
-        } else if (NORM == NORM_LN && !FOLDED && m == M) {
-            role[tt] = 1;
-        } else if (NORM == NORM_LN && !FOLDED && m == M + 1) {
-            role[tt] = 2;
-        } else {
-            role[tt] = 3;
-        }
-    }
-
-    f32x4 acc[MT][J];
-#pragma unroll
-    for (int tt = 0; tt < MT; ++tt)
-#pragma unroll
-        for (int j = 0; j < J; ++j) acc[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float S1[MT], S2[MT];
-#pragma unroll
-    for (int tt = 0; tt < MT; ++tt) S1[tt] = S2[tt] = 0.f;
-
-    const uint4 ONES = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
-    const uint4 ZERO4 = make_uint4(0u, 0u, 0u, 0u);
-
-    // stored W: 8 rows x J columns per lane; folded W'^T: J columns x 8 k per lane
-    typedef typename std::conditional<FOLDED, uint4, BT>::type LT;
-    constexpr int NL = FOLDED ? J : 8;
-    LT wr[NL];
-    uint4 xr[MT];
-    uint4 gr, br;
-
-    auto load_step = [&](int t, LT (&w)[NL], uint4 (&x)[MT], uint4& gg, uint4& bb) {
-        const int kg = t * 32 + 8 * g;
-        const int kl = kg - seg_k0;
-        if (FOLDED) {
-            const size_t K3 = (size_t)3 * d;
-#pragma unroll
-            for (int j = 0; j < NL; ++j)
-                w[j] = *reinterpret_cast<const LT*>(a.wt + (size_t)(n0 + 16 * j + cb) * K3 + kg);
-        } else {
-            const uint16_t* wp = W + (size_t)kg * d + n0 + J * cb;
-#pragma unroll
-            for (int r = 0; r < NL; ++r) w[r] = *reinterpret_cast<const LT*>(wp + (size_t)r * d);
-        }
+        // ---- per-lane role of each 16-row tile of the A operand, as bit masks:
+        // token rows take the normalised x, row M gamma, row M+1 beta, others 0.
+        // Non-token lanes load row 0 (always valid) and mask it away, so the hot
+        // loop has no divergent branches.
+        float shift[MT];
+        uint32_t tok[MT], gmk[MT], bmk[MT];
+        const uint16_t* arow[MT];
 #pragma unroll
         for (int tt = 0; tt < MT; ++tt) {
             const int m = 16 * tt + cb;
-            x[tt] = ZERO4;
-            if (role[tt] == 0) x[tt] = *reinterpret_cast<const uint4*>(hs + (size_t)m * d + kl);
+            const bool is_tok = m < M;
+            tok[tt] = is_tok ? 0xffffffffu : 0u;
+            gmk[tt] = (NORM == NORM_LN && !FOLDED && m == M) ? 0xffffffffu : 0u;
+            bmk[tt] = (NORM == NORM_LN && !FOLDED && m == M + 1) ? 0xffffffffu : 0u;
+            shift[tt] = (NORM == NORM_LN && is_tok) ? sh_shift[m] : 0.f;
+            arow[tt] = hs + (size_t)(is_tok ? m : 0) * d - seg_k0 + 8 * g;
         }
-        gg = ONES;
-        if (!FOLDED && NORM != NORM_NONE && gam != nullptr) gg = *reinterpret_cast<const uint4*>(gam + kl);
-        bb = ZERO4;
-        if (!FOLDED && NORM == NORM_LN && bet != nullptr) bb = *reinterpret_cast<const uint4*>(bet + kl);
-    };
 
-    int t = t0 + wave;
-    if (t < t1) load_step(t, wr, xr, gr, br);
-    for (; t < t1; t += DW) {
-        LT wn[NL];
-        uint4 xn[MT];
-        uint4 gn, bn;
-        const bool more = (t + DW) < t1;
-        if (more) load_step(t + DW, wn, xn, gn, bn);
-
-        // B operands: column j of the 8 x J block, 8 consecutive k
-        uint4 bf[J];
+        f32x4 acc[MT][J];
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            if constexpr (FOLDED) {
-                bf[j] = wr[j];
-            } else {
+        for (int tt = 0; tt < MT; ++tt)
+#pragma unroll
+            for (int j = 0; j < J; ++j) acc[tt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float S1[MT], S2[MT];
+#pragma unroll
+        for (int tt = 0; tt < MT; ++tt) S1[tt] = S2[tt] = 0.f;
+
+        // stored W: 8 rows x J columns per lane; folded W'^T: J columns x 8 k per lane.
+        // W (the HBM stream) is prefetched one k-step ahead; the A fragments,
+        // gamma and beta are L2 hits, loaded at the top of their own step.
+        const size_t K3 = (size_t)3 * d;
+        const uint16_t* wbase = FOLDED ? a.wt + (size_t)(n0 + cb) * K3 + 8 * g : W + (size_t)(8 * g) * d + n0 + J * cb;
+        const size_t wstep = FOLDED ? (size_t)32 : (size_t)32 * d;  // elements per k-step
+        const size_t wsub = FOLDED ? (size_t)16 * K3 : (size_t)d;   // elements between the NL loads
+        const bool has_g = !FOLDED && NORM != NORM_NONE && gam != nullptr;
+        const bool has_b = !FOLDED && NORM == NORM_LN && bet != nullptr;
+        // missing gamma / beta read a valid row of h instead and are replaced by 1 / 0
+        const uint16_t* gptr = (has_g ? gam : hs) - seg_k0 + 8 * g;
+        const uint16_t* bptr = (has_b ? bet : hs) - seg_k0 + 8 * g;
+        const uint32_t gsel = has_g ? 0xffffffffu : 0u;
+        const uint32_t bsel = has_b ? 0xffffffffu : 0u;
+
+        // Per k-step: (1) this step's A, gamma and beta loads (L2 hits);
+        // (2) transpose of this step's W, loaded one step earlier; (3) the
+        // next step's W, issued unconditionally (the last step re-reads its
+        // own rows) so the outstanding-load count is static; (4) normalise
+        // A and run the MFMAs, waiting only for (1).
+        LT wr[NL];
+        int t = tp0 + wave;
+        if (t < tp1) {
+            const uint16_t* wp = wbase + (size_t)t * wstep;
+#pragma unroll
+            for (int r = 0; r < NL; ++r) wr[r] = *reinterpret_cast<const LT*>(wp + (size_t)r * wsub);
+        }
+        for (; t < tp1; t += DW) {
+            const int k = t * 32;
+            uint4 xr[MT];
+#pragma unroll
+            for (int tt = 0; tt < MT; ++tt) xr[tt] = *reinterpret_cast<const uint4*>(arow[tt] + k);
+            uint4 gr = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
+            uint4 br = make_uint4(0u, 0u, 0u, 0u);
+            if (!FOLDED && NORM != NORM_NONE) {
+                const uint4 gl = *reinterpret_cast<const uint4*>(gptr + k);
+                gr = make_uint4((gl.x & gsel) | (0x3F803F80u & ~gsel), (gl.y & gsel) | (0x3F803F80u & ~gsel),
+                                (gl.z & gsel) | (0x3F803F80u & ~gsel), (gl.w & gsel) | (0x3F803F80u & ~gsel));
+            }
+            if (!FOLDED && NORM == NORM_LN) {
+                const uint4 bl = *reinterpret_cast<const uint4*>(bptr + k);
+                br = make_uint4(bl.x & bsel, bl.y & bsel, bl.z & bsel, bl.w & bsel);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+
+            // B operands: column j of the 8 x J block, 8 consecutive k
+            uint4 bf[J];
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                if constexpr (FOLDED) {
+                    bf[j] = wr[j];
+                } else {
+                    uint32_t q[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        const uint32_t r0 = RowVec<J>::dw(wr[2 * p], j >> 1);
+                        const uint32_t r1 = RowVec<J>::dw(wr[2 * p + 1], j >> 1);
+                        q[p] = (j & 1) ? ((r0 >> 16) | (r1 & 0xffff0000u)) : ((r0 & 0xffffu) | (r1 << 16));
+                    }
+                    bf[j] = make_uint4(q[0], q[1], q[2], q[3]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                const int tn = (t + DW) < tp1 ? t + DW : t;
+                const uint16_t* wp = wbase + (size_t)tn * wstep;
+#pragma unroll
+                for (int r = 0; r < NL; ++r) wr[r] = *reinterpret_cast<const LT*>(wp + (size_t)r * wsub);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+
+            float gf[8];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t w = u4get(gr, p);
+                gf[2 * p] = bf_lo(w);
+                gf[2 * p + 1] = bf_hi(w);
+            }
+#pragma unroll
+            for (int tt = 0; tt < MT; ++tt) {
                 uint32_t q[4];
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
-                    const uint32_t r0 = RowVec<J>::dw(wr[2 * p], j >> 1);
-                    const uint32_t r1 = RowVec<J>::dw(wr[2 * p + 1], j >> 1);
-                    q[p] = (j & 1) ? ((r0 >> 16) | (r1 & 0xffff0000u)) : ((r0 & 0xffffu) | (r1 << 16));
+                    const uint32_t w = u4get(xr[tt], p) & tok[tt];
+                    if (NORM == NORM_NONE) {
+                        q[p] = w;
+                    } else {
+                        float x0 = bf_lo(w), x1 = bf_hi(w);
+                        if (NORM == NORM_LN) {
+                            x0 -= shift[tt];
+                            x1 -= shift[tt];
+                            S1[tt] += x0 + x1;
+                        }
+                        S2[tt] += x0 * x0 + x1 * x1;
+                        if (FOLDED) {
+                            q[p] = w;  // raw x feeds the MFMA against gamma * W
+                        } else {
+                            const uint32_t pk = pack_bf2(x0 * gf[2 * p], x1 * gf[2 * p + 1]) & tok[tt];
+                            q[p] = pk | (u4get(gr, p) & gmk[tt]) | (u4get(br, p) & bmk[tt]);
+                        }
+                    }
                 }
-                bf[j] = make_uint4(q[0], q[1], q[2], q[3]);
-            }
-        }
-        // gamma of this lane's 8 k values
-        float gf[8];
+                const uint4 af = make_uint4(q[0], q[1], q[2], q[3]);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t w = u4get(gr, p);
-            gf[2 * p] = bf_lo(w);
-            gf[2 * p + 1] = bf_hi(w);
+                for (int j = 0; j < J; ++j) acc[tt][j] = mfma16x16x32(af, bf[j], acc[tt][j]);
+            }
+
         }
+
+        // ---- piece statistics: the 4 lane groups, then the waves (fixed order below)
 #pragma unroll
         for (int tt = 0; tt < MT; ++tt) {
-            uint4 af;
-            if (NORM == NORM_NONE) {
-                af = xr[tt];
-            } else if (FOLDED) {
-                // raw x feeds the MFMA; only the statistics are formed here
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const uint32_t w = u4get(xr[tt], p);
-                    float x0 = bf_lo(w), x1 = bf_hi(w);
-                    if (NORM == NORM_LN) {
-                        x0 -= shift[tt];
-                        x1 -= shift[tt];
-                        S1[tt] += x0 + x1;
-                    }
-                    S2[tt] += x0 * x0 + x1 * x1;
-                }
-                af = xr[tt];
-            } else {
-                uint32_t q[4];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const uint32_t w = u4get(xr[tt], p);
-                    float x0 = bf_lo(w), x1 = bf_hi(w);
-                    if (NORM == NORM_LN) {
-                        x0 -= shift[tt];
-                        x1 -= shift[tt];
-                        S1[tt] += x0 + x1;
-                    }
-                    S2[tt] += x0 * x0 + x1 * x1;
-                    q[p] = pack_bf2(x0 * gf[2 * p], x1 * gf[2 * p + 1]);
-                }
-                af = make_uint4(q[0], q[1], q[2], q[3]);
-                if (NORM == NORM_LN) {
-                    // padding lanes hold x = 0 and shift = 0, so their sums stay 0
-                    af = role[tt] == 0 ? af : (role[tt] == 1 ? gr : (role[tt] == 2 ? br : ZERO4));
-                }
+            const float a1 = group4_sum(S1[tt]);
+            const float a2 = group4_sum(S2[tt]);
+            const int m = 16 * tt + cb;
+            if (g == 0 && m < M) {
+                sh_s1[wave][m] = a1;
+                sh_s2[wave][m] = a2;
             }
-#pragma unroll
-            for (int j = 0; j < J; ++j) acc[tt][j] = mfma16x16x32(af, bf[j], acc[tt][j]);
         }
 
-        if (more) {
+        // ---- pairwise sum of the 8 wave tiles in fragment order:
+        //      ((w0 + w4) + (w2 + w6)) + ((w1 + w5) + (w3 + w7))
+        f32x4* buf = reinterpret_cast<f32x4*>(sh_big);
 #pragma unroll
-            for (int r = 0; r < NL; ++r) wr[r] = wn[r];
+        for (int half = 4; half >= 1; half >>= 1) {
+            if (wave >= half && wave < 2 * half) {
+                f32x4* dst = buf + (wave - half) * FR * 64;
 #pragma unroll
-            for (int tt = 0; tt < MT; ++tt) xr[tt] = xn[tt];
-            gr = gn;
-            br = bn;
+                for (int tt = 0; tt < MT; ++tt)
+#pragma unroll
+                    for (int j = 0; j < J; ++j) dst[(tt * J + j) * 64 + lane] = acc[tt][j];
+            }
+            __syncthreads();
+            if (wave < half) {
+                const f32x4* src = buf + wave * FR * 64;
+#pragma unroll
+                for (int tt = 0; tt < MT; ++tt)
+#pragma unroll
+                    for (int j = 0; j < J; ++j) acc[tt][j] += src[(tt * J + j) * 64 + lane];
+            }
+            __syncthreads();
         }
+        // wave 0 holds the workgroup's tile; lay it out row-major for coalesced stores
+        float* rowmaj = sh_big;
+        if (wave == 0) {
+#pragma unroll
+            for (int tt = 0; tt < MT; ++tt)
+#pragma unroll
+                for (int j = 0; j < J; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        rowmaj[(16 * tt + 4 * g + e) * NW + dcol<J, FOLDED>(j, cb)] = acc[tt][j][e];
+        }
+        __syncthreads();
+
+        const int slot = (b * ks + c) * DECODE_SLOTS + pi;
+        float4* part = reinterpret_cast<float4*>(a.part + (size_t)slot * TILE);
+        const float4* src4 = reinterpret_cast<const float4*>(rowmaj);
+        for (int v = tid; v < Mst * NW / 4; v += DTHREADS) part[v] = src4[v];
+        if (NORM != NORM_NONE) {
+            float* st = a.stats + (size_t)slot * DECODE_MAX_M * 3;
+            for (int m = tid; m < M; m += DTHREADS) {
+                const float v1 = ((sh_s1[0][m] + sh_s1[4][m]) + (sh_s1[2][m] + sh_s1[6][m])) +
+                                 ((sh_s1[1][m] + sh_s1[5][m]) + (sh_s1[3][m] + sh_s1[7][m]));
+                const float v2 = ((sh_s2[0][m] + sh_s2[4][m]) + (sh_s2[2][m] + sh_s2[6][m])) +
+                                 ((sh_s2[1][m] + sh_s2[5][m]) + (sh_s2[3][m] + sh_s2[7][m]));
+                st[3 * m + 0] = NORM == NORM_LN ? sh_shift[m] : 0.f;
+                st[3 * m + 1] = v1;
+                st[3 * m + 2] = v2;
+            }
+        }
+        __syncthreads();  // LDS is reused by the next piece
     }
 
-    // ---- per-row chunk statistics: sum over the 4 lane groups, then the waves
-#pragma unroll
-    for (int tt = 0; tt < MT; ++tt) {
-        const float a1 = group4_sum(S1[tt]);
-        const float a2 = group4_sum(S2[tt]);
-        const int m = 16 * tt + cb;
-        if (g == 0 && m < M) {
-            sh_s1[wave][m] = a1;
-            sh_s2[wave][m] = a2;
-        }
-    }
-    // ---- sum of the four waves' tiles in a fixed order: (w0 + w2) + (w1 + w3).
-    // All waves share the lane <-> element mapping of the MFMA output, so the
-    // tiles are exchanged in that "fragment order" with 16-byte LDS accesses.
-    constexpr int FR = MT * J;  // f32x4 fragments per lane
-    f32x4* buf0 = reinterpret_cast<f32x4*>(sh_big);
-    f32x4* buf1 = buf0 + FR * 64;
-    if (wave >= 2) {
-        f32x4* dst = wave == 2 ? buf0 : buf1;
-#pragma unroll
-        for (int tt = 0; tt < MT; ++tt)
-#pragma unroll
-            for (int j = 0; j < J; ++j) dst[(tt * J + j) * 64 + lane] = acc[tt][j];
-    }
-    __syncthreads();
-    if (wave < 2) {
-        const f32x4* src = wave == 0 ? buf0 : buf1;
-#pragma unroll
-        for (int tt = 0; tt < MT; ++tt)
-#pragma unroll
-            for (int j = 0; j < J; ++j) acc[tt][j] += src[(tt * J + j) * 64 + lane];
-    }
-    __syncthreads();
-    if (wave == 1) {
-#pragma unroll
-        for (int tt = 0; tt < MT; ++tt)
-#pragma unroll
-            for (int j = 0; j < J; ++j) buf0[(tt * J + j) * 64 + lane] = acc[tt][j];
-    }
-    __syncthreads();
-
-    const int slot = b * nchunks + c;
-    f32x4* part = reinterpret_cast<f32x4*>(a.part) + (size_t)slot * FR * 64;
-    if (wave == 0) {
-#pragma unroll
-        for (int tt = 0; tt < MT; ++tt)
-#pragma unroll
-            for (int j = 0; j < J; ++j) part[(tt * J + j) * 64 + lane] = acc[tt][j] + buf0[(tt * J + j) * 64 + lane];
-    }
-    if (NORM != NORM_NONE) {
-        float* st = a.stats + (size_t)slot * DECODE_MAX_M * 3;
-        for (int m = tid; m < M; m += DTHREADS) {
-            const float v1 = (sh_s1[0][m] + sh_s1[2][m]) + (sh_s1[1][m] + sh_s1[3][m]);
-            const float v2 = (sh_s2[0][m] + sh_s2[2][m]) + (sh_s2[1][m] + sh_s2[3][m]);
-            st[3 * m + 0] = NORM == NORM_LN ? sh_shift[m] : 0.f;
-            st[3 * m + 1] = v1;
-            st[3 * m + 2] = v2;
-        }
-    }
-    __threadfence();
+    // Publish: every wave waits until its own stores have reached L2 (the
+    // workgroup barrier alone does not wait for them), then thread 0's
+    // counter increment is a release at agent scope: one L2 write-back per
+    // workgroup.  Only the last arriver acquires (one L2 invalidate per
+    // column block) before reading the other workgroups' tiles.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(a.counters + b, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        sh_last = (old == nchunks - 1);
+        const int old = __hip_atomic_fetch_add(a.counters + b, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        sh_last = (old == ks - 1);
     }
     __syncthreads();
     if (!sh_last) return;
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-    // ---- last arriver of column block b: statistics of every state, then the sum
-    float* sh_delta = sh_big;  // [nchunks][64]: mu_s - K_c (LayerNorm)
+    // ================= last arriver of column block b =================
+    // Pieces of this column block by state: state s is covered by chunks
+    // chunk_of(s*TS) .. chunk_of((s+1)*TS - 1), at most PPS of them; every
+    // table below is indexed by compile-time (s, q), so it lives in registers.
+    auto chunk_of = [&](int tt) { return ((tt + 1) * ks - 1) / T; };
+    int pslot[3][PPS], plen[3][PPS];
+    bool pval[3][PPS];
+#pragma unroll
+    for (int ss = 0; ss < 3; ++ss) {
+        const int c0 = chunk_of(ss * TS), c1 = chunk_of((ss + 1) * TS - 1);
+#pragma unroll
+        for (int q = 0; q < PPS; ++q) {
+            const int cc = c0 + q;
+            const int a0 = (cc * T) / ks, a1 = ((cc + 1) * T) / ks;
+            pval[ss][q] = cc <= c1;
+            pslot[ss][q] = pval[ss][q] ? (b * ks + cc) * DECODE_SLOTS + (ss - a0 / TS) : 0;
+            plen[ss][q] = pval[ss][q] ? 32 * (min(a1, (ss + 1) * TS) - max(a0, ss * TS)) : 0;
+        }
+    }
+
+    // statistics of every state and token (float64 combination of the pieces)
+    float* sh_delta = sh_big;  // [3 * PPS][64]: mu_s - K_p
     for (int m = tid; m < M; m += DTHREADS) {
+#pragma unroll
         for (int ss = 0; ss < 3; ++ss) {
-            double r = 1.0;
+            float K[PPS], s1[PPS], s2[PPS];
+#pragma unroll
+            for (int q = 0; q < PPS; ++q) {
+                K[q] = s1[q] = s2[q] = 0.f;
+                if (NORM != NORM_NONE && pval[ss][q]) {
+                    const float* st = a.stats + ((size_t)pslot[ss][q] * DECODE_MAX_M + m) * 3;
+                    K[q] = st[0];
+                    s1[q] = st[1];
+                    s2[q] = st[2];
+                }
+            }
+            double r = 1.0, mu = 0.0;
             if (NORM == NORM_LN) {
                 double sum = 0.0;
-                for (int cc = ss * kps; cc < (ss + 1) * kps; ++cc) {
-                    const float* st = a.stats + ((size_t)(b * nchunks + cc) * DECODE_MAX_M + m) * 3;
-                    const int cjj = cc - ss * kps;
-                    const double n_c = 32.0 * (double)(((cjj + 1) * TS) / kps - (cjj * TS) / kps);
-                    sum += n_c * (double)st[0] + (double)st[1];
-                }
-                const double mu = sum / (double)d;
+#pragma unroll
+                for (int q = 0; q < PPS; ++q) sum += (double)plen[ss][q] * (double)K[q] + (double)s1[q];
+                mu = sum / (double)d;
                 double m2 = 0.0;
-                for (int cc = ss * kps; cc < (ss + 1) * kps; ++cc) {
-                    const float* st = a.stats + ((size_t)(b * nchunks + cc) * DECODE_MAX_M + m) * 3;
-                    const int cjj = cc - ss * kps;
-                    const double n_c = 32.0 * (double)(((cjj + 1) * TS) / kps - (cjj * TS) / kps);
-                    const double dl = mu - (double)st[0];
-                    m2 += (double)st[2] - 2.0 * dl * (double)st[1] + n_c * dl * dl;
-                    sh_delta[cc * DECODE_MAX_M + m] = (float)dl;
+#pragma unroll
+                for (int q = 0; q < PPS; ++q) {
+                    const double dl = mu - (double)K[q];
+                    if (pval[ss][q]) m2 += (double)s2[q] - 2.0 * dl * (double)s1[q] + (double)plen[ss][q] * dl * dl;
+                    sh_delta[(ss * PPS + q) * DECODE_MAX_M + m] = (float)dl;
                 }
-                sh_mu[ss][m] = (float)mu;
                 r = 1.0 / sqrt(m2 / (double)d + (double)a.eps);
             } else if (NORM == NORM_RMS) {
                 double sq = 0.0;
-                for (int cc = ss * kps; cc < (ss + 1) * kps; ++cc)
-                    sq += (double)a.stats[((size_t)(b * nchunks + cc) * DECODE_MAX_M + m) * 3 + 2];
+#pragma unroll
+                for (int q = 0; q < PPS; ++q) sq += (double)s2[q];
                 r = 1.0 / sqrt(sq / (double)d + (double)a.eps);
             }
             sh_r[ss][m] = (float)r;
+            sh_mu[ss][m] = (float)mu;
         }
     }
     __syncthreads();
 
-    // Each thread takes one fragment (4 consecutive rows of one column) at a
-    // time, reading every chunk's partial in a fixed order.
-    const f32x4* pbase = reinterpret_cast<const f32x4*>(a.part) + (size_t)b * nchunks * FR * 64;
-    // fragment holding (row, column): row = 16*tt + 4*(lane>>4) + e, column = dcol(j, lane&15)
-    const int Mu = M, Mc = M + 1;
-    const int u_tt = Mu >> 4, u_g = (Mu & 15) >> 2, u_e = Mu & 3;
-    const int c_tt = Mc >> 4, c_g = (Mc & 15) >> 2, c_e = Mc & 3;
-    for (int f = tid; f < FR * 64; f += DTHREADS) {
-        const int tt = f / (J * 64);
-        const int j = (f / 64) % J;
-        const int ln = f & 63;
-        const int row0 = 16 * tt + 4 * (ln >> 4);
-        if (row0 >= M) continue;
-        const int n = dcol<J, FOLDED>(j, ln & 15);
-        float y[4] = {0.f, 0.f, 0.f, 0.f};
-        float cterm = 0.f;
+    // outputs: thread -> column n, rows rg, rg + RG, ...; every load is issued first
+    const int n = tid % NW;
+    const int rg = tid / NW;
+    float P[3][PPS][RPT];
+    float U[3][PPS];
+    float add = 0.f;
+#pragma unroll
+    for (int ss = 0; ss < 3; ++ss)
+#pragma unroll
+        for (int q = 0; q < PPS; ++q) {
+            const float* base = a.part + (size_t)pslot[ss][q] * TILE;
+            U[ss][q] = 0.f;
+            if (NORM == NORM_LN && !FOLDED && pval[ss][q]) {
+                U[ss][q] = base[M * NW + n];
+                add += base[(M + 1) * NW + n];
+            }
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int m = rg + RG * i;
+                P[ss][q][i] = (pval[ss][q] && m < M) ? base[m * NW + n] : 0.f;
+            }
+        }
+    float usum[3] = {0.f, 0.f, 0.f};
+    if (FOLDED) {
+        if (NORM == NORM_LN)
+#pragma unroll
+            for (int ss = 0; ss < 3; ++ss) usum[ss] = a.u[(size_t)ss * d + n0 + n];
+        add += a.c[n0 + n];
+    } else if (a.bias != nullptr) {
+        add += bf_one(a.bias[n0 + n]);
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int m = rg + RG * i;
+        if (m >= M) continue;
+        float y = 0.f;
+#pragma unroll
         for (int ss = 0; ss < 3; ++ss) {
-            float ys[4] = {0.f, 0.f, 0.f, 0.f};
-            for (int cc = ss * kps; cc < (ss + 1) * kps; ++cc) {
-                const f32x4* p = pbase + (size_t)cc * FR * 64;
-                const f32x4 v = p[f];
-                if (NORM == NORM_LN && !FOLDED) {
-                    const float U = p[(u_tt * J + j) * 64 + 16 * u_g + (ln & 15)][u_e];
-                    cterm += p[(c_tt * J + j) * 64 + 16 * c_g + (ln & 15)][c_e];
+            float ys = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int m = row0 + e;
-                        const float dl = m < M ? sh_delta[cc * DECODE_MAX_M + m] : 0.f;
-                        ys[e] += v[e] - dl * U;
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) ys[e] += v[e];
-                }
+            for (int q = 0; q < PPS; ++q) {
+                float v = P[ss][q][i];
+                if (NORM == NORM_LN && !FOLDED) v -= sh_delta[(ss * PPS + q) * DECODE_MAX_M + m] * U[ss][q];
+                ys += v;
             }
-            if (FOLDED && NORM == NORM_LN) {
-                const float us = a.u[(size_t)ss * d + n0 + n];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int m = row0 + e;
-                    ys[e] -= (m < M ? sh_mu[ss][m] : 0.f) * us;
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int m = row0 + e;
-                const float r = (NORM == NORM_NONE || m >= M) ? 1.f : sh_r[ss][m];
-                y[e] += r * ys[e];
-            }
+            if (FOLDED && NORM == NORM_LN) ys -= sh_mu[ss][m] * usum[ss];
+            y += (NORM == NORM_NONE) ? ys : sh_r[ss][m] * ys;
         }
-        float add = cterm;
-        if (FOLDED) {
-            add += a.c[n0 + n];
-        } else if (a.bias != nullptr) {
-            add += bf_one(a.bias[n0 + n]);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int m = row0 + e;
-            if (m < M) {
-                const float v = y[e] + add;
-                a.out[(size_t)m * d + n0 + n] = __builtin_bit_cast(uint16_t, (__bf16)v);
-            }
-        }
+        a.out[(size_t)m * d + n0 + n] = __builtin_bit_cast(uint16_t, (__bf16)(y + add));
     }
     if (tid == 0) a.counters[b] = 0;
 }
@@ -454,14 +485,14 @@ DecodePlan plan_decode(int M, int d, int norm, bool folded) {
     p.J = p.MT <= 2 ? 8 : 4;
     if (d % (16 * p.J) != 0) p.J = 4;
     p.nb = d / (16 * p.J);
-    const int TS = d / 32;
-    int kps = (768 + 3 * p.nb - 1) / (3 * p.nb);
-    if (kps < 1) kps = 1;
-    const int kmax = TS / DW > 0 ? TS / DW : 1;
-    if (kps > kmax) kps = kmax;
-    if (kps > DECODE_MAX_KPS) kps = DECODE_MAX_KPS;
-    p.kps = kps;
-    const size_t slots = (size_t)p.nb * 3 * kps;
+    const int T = 3 * (d / 32);
+    // about one 8-wave workgroup per CU, each wave at least two k-steps per chunk
+    int ks = (256 + p.nb / 2) / p.nb;
+    if (ks < 1) ks = 1;
+    if (ks > DECODE_MAX_KS) ks = DECODE_MAX_KS;
+    while (ks > 1 && T / ks < 2 * DW) --ks;
+    p.kps = ks;
+    const size_t slots = (size_t)p.nb * ks * DECODE_SLOTS;
     p.counters_bytes = ((size_t)p.nb * sizeof(int) + 255) / 256 * 256;
     p.stats_bytes = (slots * DECODE_MAX_M * 3 * sizeof(float) + 255) / 256 * 256;
     p.part_bytes = (slots * (size_t)p.MT * 16 * 16 * p.J * sizeof(float) + 255) / 256 * 256;
@@ -470,7 +501,7 @@ DecodePlan plan_decode(int M, int d, int norm, bool folded) {
 
 template <int NORM, int J, int MT, bool FOLDED>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
-    const int grid = a.nb * 3 * a.kps;
+    const int grid = a.nb * a.kps;
     decode_kernel<NORM, J, MT, FOLDED><<<grid, DTHREADS, 0, st>>>(a);
     return hipGetLastError();
 }

@@ -42,6 +42,22 @@ constexpr int DECODE_MAX_M = 64;
 DecodePlan plan_decode(int M, int d, int norm, bool folded);
 hipError_t launch_decode(const DecodeArgs& a, int norm, bool folded, const DecodePlan& p, hipStream_t st);
 
+// Small-M path on the folded weight: one workgroup per 16 columns over the
+// whole K, statistics from the row-statistics pass (no workspace, no atomics).
+struct DecodeColsArgs {
+    const uint16_t* h[3];
+    const uint16_t* wt;   // [d, 3d] folded + transposed
+    const float* u;       // [3, d]
+    const float* c;       // [d]
+    const float* mu;      // [3, M]
+    const float* rstd;    // [3, M]
+    uint16_t* out;        // [M, d]
+    int M, d;
+    float eps;
+    bool instats;         // statistics in the kernel (M <= 16) instead of mu / rstd
+};
+hipError_t launch_decode_cols(const DecodeColsArgs& a, int norm, hipStream_t st);
+
 // -------------------------------------------------------------- fold prepare
 hipError_t launch_fold_prepare(int d, int norm, const uint16_t* const gamma[3], const uint16_t* const beta[3],
                                const uint16_t* W, const uint16_t* bias, uint16_t* wt, float* u, float* c,

@@ -124,7 +124,7 @@ int eagle31_fuse_ws(const void* h_low, const void* h_mid, const void* h_high, in
  *             n*3d + k equals bf16_rne(gamma_s[k - s*d] * W[k, n]) for
  *             LAYERNORM / RMSNORM and W[k, n] for NONE;
  *   u         float32 [3, d]: u[s][n] = sum over k in state s of w_folded(n, k)
- *             (from the stored, rounded values; zeros for NONE);
+ *             (from the stored, rounded values; unused by NONE);
  *   c         float32 [d]: c[n] = bias[n] + sum_s sum_k beta_s[k] W[s*d + k, n]
  *             (the beta term for LAYERNORM only).
  * Then, for the same norm_kind,
