@@ -1,10 +1,11 @@
 // C ABI of the fused per-state norm + FC (declared in include/eagle31.h).
 //
 // Every argument check runs on the host before the first HIP call; a failed
-// check enqueues nothing.  Dispatch: M <= 64 runs the single-launch decode
-// kernel on W in its stored layout (or on the folded W'^T); larger M runs the
-// row-statistics pass and the folded GEMM, preparing W'^T, u and c into the
-// workspace first when the caller passed the stored W.
+// check enqueues nothing.  Dispatch: M <= 64 runs a single-launch decode
+// kernel, on W in its stored layout or on the folded weight tiles (both
+// split-K with in-kernel statistics); larger M runs the row-statistics pass and the folded GEMM,
+// preparing W', u and c into the workspace first when the caller passed the
+// stored W.
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -84,26 +85,23 @@ size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 // rest) the previous call used.
 constexpr size_t COUNTER_REGION = 16384;  // 4096 counters
 constexpr int MAX_COUNTERS = (int)(COUNTER_REGION / sizeof(int));
-// the folded weight's column-block kernel reads all tokens per column block:
-// it wins while the token fragments are few; beyond that the split-K kernel does
-constexpr int64_t DECODE_COLS_MAX_M = 16;
-
 WsLayout layout_for(int64_t M, int64_t d, int norm, bool folded) {
     WsLayout L;
     if (M <= 0) return L;
     L.counters = 0;
     L.counters_bytes = COUNTER_REGION;
     size_t off = COUNTER_REGION;
-    if (M <= DECODE_COLS_MAX_M && folded) {
-        L.mu = off;
-        off += up256((size_t)3 * M * sizeof(float));
-        L.rstd = off;
-        off += up256((size_t)3 * M * sizeof(float));
+    if (M <= DECODE_MAX_M && folded) {
+        const GemvPlan p = plan_gemv((int)M, (int)d);
+        L.stats = off;
+        off += up256(p.stats_bytes);
+        L.part = off;
+        off += up256(p.part_bytes);
         L.total = off;
         return L;
     }
     if (M <= DECODE_MAX_M) {
-        const DecodePlan p = plan_decode((int)M, (int)d, norm, folded);
+        const DecodePlan p = plan_decode((int)M, (int)d, norm);
         L.stats = off;
         off += up256(p.stats_bytes);
         L.part = off;
@@ -192,32 +190,29 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
         for (int s = 0; s < 3; ++s) b[s] = static_cast<const uint16_t*>(beta[s]);
 
     hipError_t e;
-    if (M <= DECODE_COLS_MAX_M && folded) {
-        float* mu = at<float>(ws, L.mu);
-        float* rstd = at<float>(ws, L.rstd);
-        const bool instats = M <= 16;
-        if (norm != NORM_NONE && !instats) {
-            e = launch_row_stats(h[0], h[1], h[2], (int)M, (int)d, norm, eps, mu, rstd, st);
-            if (e != hipSuccess) return hip_fail(e);
-        }
-        DecodeColsArgs a;
-        a.eps = eps;
-        a.instats = instats;
+    if (M <= DECODE_MAX_M && folded) {
+        const GemvPlan p = plan_gemv((int)M, (int)d);
+        if (p.kps == 0 || d / 64 > MAX_COUNTERS) return EAGLE31_ERR_SHAPE;
+        GemvArgs a;
         for (int s = 0; s < 3; ++s) a.h[s] = h[s];
-        a.wt = static_cast<const uint16_t*>(wt);
+        a.wp = static_cast<const uint16_t*>(wt);
         a.u = u;
         a.c = c;
-        a.mu = mu;
-        a.rstd = rstd;
         a.out = static_cast<uint16_t*>(out);
         a.M = (int)M;
         a.d = (int)d;
-        e = launch_decode_cols(a, norm, st);
+        a.eps = eps;
+        a.kps = p.kps;
+        a.waves = p.waves;
+        a.counters = at<int>(ws, L.counters);
+        a.stats = at<float>(ws, L.stats);
+        a.part = at<float>(ws, L.part);
+        e = launch_gemv(a, norm, p, st);
         if (e != hipSuccess) return hip_fail(e);
         return EAGLE31_OK;
     }
     if (M <= DECODE_MAX_M) {
-        const DecodePlan p = plan_decode((int)M, (int)d, norm, folded);
+        const DecodePlan p = plan_decode((int)M, (int)d, norm);
         if (p.nb > MAX_COUNTERS) return EAGLE31_ERR_SHAPE;
         DecodeArgs a;
         for (int s = 0; s < 3; ++s) {
@@ -226,10 +221,7 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
             a.beta[s] = b[s];
         }
         a.W = static_cast<const uint16_t*>(W);
-        a.wt = static_cast<const uint16_t*>(wt);
-        a.u = u;
-        a.c = c;
-        a.bias = folded ? nullptr : static_cast<const uint16_t*>(bias);
+        a.bias = static_cast<const uint16_t*>(bias);
         a.out = static_cast<uint16_t*>(out);
         a.M = (int)M;
         a.d = (int)d;
@@ -239,7 +231,7 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
         a.counters = at<int>(ws, L.counters);
         a.stats = at<float>(ws, L.stats);
         a.part = at<float>(ws, L.part);
-        e = launch_decode(a, norm, folded, p, st);
+        e = launch_decode(a, norm, p, st);
         if (e != hipSuccess) return hip_fail(e);
         return EAGLE31_OK;
     }

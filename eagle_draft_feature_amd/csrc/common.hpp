@@ -31,6 +31,16 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const uint4& a, const uint4& b, co
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Stores / loads performed at the device coherence point (agent-scope
+// relaxed atomics), for values handed from one workgroup to another within a
+// launch without writing back or invalidating a whole L2.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);

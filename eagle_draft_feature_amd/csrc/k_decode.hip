@@ -16,8 +16,8 @@
 //    row-major layout: each lane loads 8 consecutive rows x J consecutive
 //    columns and transposes that 8 x J block in registers into J MFMA B
 //    operands (8 consecutive k of one column each): half a byte-permute per
-//    element.  The folded variant streams W'^T instead, whose 16-byte rows
-//    are MFMA operands as loaded.
+//    element.  (The folded weight has its own kernel: its tiles are MFMA
+//    operands as loaded.)
 //  * A chunk that crosses a state boundary is processed as pieces, one per
 //    state; every piece has its own partial tile and statistics.
 //  * The A operand is built on the fly from the raw hidden states: LayerNorm
@@ -74,16 +74,11 @@ __device__ __forceinline__ uint32_t u4get(const uint4& v, int i) {
     return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
 }
 
-// rows of the A operand after the tokens: gamma and beta (LayerNorm on the
-// stored W; the folded variant gets u and c from the prepare step instead)
-template <int NORM, bool FOLDED>
-__host__ __device__ constexpr int param_rows() { return (NORM == NORM_LN && !FOLDED) ? 2 : 0; }
+// rows of the A operand after the tokens: gamma and beta (LayerNorm)
+template <int NORM>
+__host__ __device__ constexpr int param_rows() { return NORM == NORM_LN ? 2 : 0; }
 
-// column of MFMA block j for lane column cb inside the block of 16*J columns
-template <int J, bool FOLDED>
-__device__ __forceinline__ int dcol(int j, int cb) { return FOLDED ? 16 * j + cb : J * cb + j; }
-
-template <int NORM, int J, int MT, bool FOLDED>
+template <int NORM, int J, int MT>
 __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
     constexpr int NW = 16 * J;
     constexpr int ROWS = 16 * MT;
@@ -92,9 +87,8 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
     constexpr int RG = DTHREADS / NW;     // row groups of the reducer
     constexpr int MAXROWS = ROWS < DECODE_MAX_M ? ROWS : DECODE_MAX_M;
     constexpr int RPT = (MAXROWS + RG - 1) / RG;  // reducer rows per thread
-    typedef typename RowVec<J>::T BT;
-    typedef typename std::conditional<FOLDED, uint4, BT>::type LT;
-    constexpr int NL = FOLDED ? J : 8;
+    typedef typename RowVec<J>::T LT;
+    constexpr int NL = 8;
 
     const int nb = a.nb, ks = a.kps, M = a.M, d = a.d;
     const int b = blockIdx.x % nb;
@@ -103,7 +97,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
     const int T = 3 * TS;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, cb = lane & 15;
     const int n0 = b * NW;
-    const int Mst = M + param_rows<NORM, FOLDED>();
+    const int Mst = M + param_rows<NORM>();
     const uint16_t* __restrict__ W = a.W;
 
     // big: 4 wave tiles for the pairwise sums; reused for the row-major tile
@@ -115,7 +109,6 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
     __shared__ float sh_s1[DW][DECODE_MAX_M];
     __shared__ float sh_s2[DW][DECODE_MAX_M];
     __shared__ float sh_r[3][DECODE_MAX_M];
-    __shared__ float sh_mu[3][DECODE_MAX_M];
     __shared__ int sh_last;
 
     // chunk c covers k-steps [t0c, t1c); piece pi is its part in state s_first + pi
@@ -158,8 +151,8 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
             const int m = 16 * tt + cb;
             const bool is_tok = m < M;
             tok[tt] = is_tok ? 0xffffffffu : 0u;
-            gmk[tt] = (NORM == NORM_LN && !FOLDED && m == M) ? 0xffffffffu : 0u;
-            bmk[tt] = (NORM == NORM_LN && !FOLDED && m == M + 1) ? 0xffffffffu : 0u;
+            gmk[tt] = (NORM == NORM_LN && m == M) ? 0xffffffffu : 0u;
+            bmk[tt] = (NORM == NORM_LN && m == M + 1) ? 0xffffffffu : 0u;
             shift[tt] = (NORM == NORM_LN && is_tok) ? sh_shift[m] : 0.f;
             arow[tt] = hs + (size_t)(is_tok ? m : 0) * d - seg_k0 + 8 * g;
         }
@@ -173,15 +166,14 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int tt = 0; tt < MT; ++tt) S1[tt] = S2[tt] = 0.f;
 
-        // stored W: 8 rows x J columns per lane; folded W'^T: J columns x 8 k per lane.
+        // W: 8 rows x J columns per lane.
         // W (the HBM stream) is prefetched one k-step ahead; the A fragments,
         // gamma and beta are L2 hits, loaded at the top of their own step.
-        const size_t K3 = (size_t)3 * d;
-        const uint16_t* wbase = FOLDED ? a.wt + (size_t)(n0 + cb) * K3 + 8 * g : W + (size_t)(8 * g) * d + n0 + J * cb;
-        const size_t wstep = FOLDED ? (size_t)32 : (size_t)32 * d;  // elements per k-step
-        const size_t wsub = FOLDED ? (size_t)16 * K3 : (size_t)d;   // elements between the NL loads
-        const bool has_g = !FOLDED && NORM != NORM_NONE && gam != nullptr;
-        const bool has_b = !FOLDED && NORM == NORM_LN && bet != nullptr;
+        const uint16_t* wbase = W + (size_t)(8 * g) * d + n0 + J * cb;
+        const size_t wstep = (size_t)32 * d;  // elements per k-step
+        const size_t wsub = (size_t)d;        // elements between the NL loads
+        const bool has_g = NORM != NORM_NONE && gam != nullptr;
+        const bool has_b = NORM == NORM_LN && bet != nullptr;
         // missing gamma / beta read a valid row of h instead and are replaced by 1 / 0
         const uint16_t* gptr = (has_g ? gam : hs) - seg_k0 + 8 * g;
         const uint16_t* bptr = (has_b ? bet : hs) - seg_k0 + 8 * g;
@@ -207,12 +199,12 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
             for (int tt = 0; tt < MT; ++tt) xr[tt] = *reinterpret_cast<const uint4*>(arow[tt] + k);
             uint4 gr = make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u);
             uint4 br = make_uint4(0u, 0u, 0u, 0u);
-            if (!FOLDED && NORM != NORM_NONE) {
+            if (NORM != NORM_NONE) {
                 const uint4 gl = *reinterpret_cast<const uint4*>(gptr + k);
                 gr = make_uint4((gl.x & gsel) | (0x3F803F80u & ~gsel), (gl.y & gsel) | (0x3F803F80u & ~gsel),
                                 (gl.z & gsel) | (0x3F803F80u & ~gsel), (gl.w & gsel) | (0x3F803F80u & ~gsel));
             }
-            if (!FOLDED && NORM == NORM_LN) {
+            if (NORM == NORM_LN) {
                 const uint4 bl = *reinterpret_cast<const uint4*>(bptr + k);
                 br = make_uint4(bl.x & bsel, bl.y & bsel, bl.z & bsel, bl.w & bsel);
             }
@@ -222,18 +214,14 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
             uint4 bf[J];
 #pragma unroll
             for (int j = 0; j < J; ++j) {
-                if constexpr (FOLDED) {
-                    bf[j] = wr[j];
-                } else {
-                    uint32_t q[4];
+                uint32_t q[4];
 #pragma unroll
-                    for (int p = 0; p < 4; ++p) {
-                        const uint32_t r0 = RowVec<J>::dw(wr[2 * p], j >> 1);
-                        const uint32_t r1 = RowVec<J>::dw(wr[2 * p + 1], j >> 1);
-                        q[p] = (j & 1) ? ((r0 >> 16) | (r1 & 0xffff0000u)) : ((r0 & 0xffffu) | (r1 << 16));
-                    }
-                    bf[j] = make_uint4(q[0], q[1], q[2], q[3]);
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t r0 = RowVec<J>::dw(wr[2 * p], j >> 1);
+                    const uint32_t r1 = RowVec<J>::dw(wr[2 * p + 1], j >> 1);
+                    q[p] = (j & 1) ? ((r0 >> 16) | (r1 & 0xffff0000u)) : ((r0 & 0xffffu) | (r1 << 16));
                 }
+                bf[j] = make_uint4(q[0], q[1], q[2], q[3]);
             }
             __builtin_amdgcn_sched_barrier(0);
             {
@@ -267,12 +255,8 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
                             S1[tt] += x0 + x1;
                         }
                         S2[tt] += x0 * x0 + x1 * x1;
-                        if (FOLDED) {
-                            q[p] = w;  // raw x feeds the MFMA against gamma * W
-                        } else {
-                            const uint32_t pk = pack_bf2(x0 * gf[2 * p], x1 * gf[2 * p + 1]) & tok[tt];
-                            q[p] = pk | (u4get(gr, p) & gmk[tt]) | (u4get(br, p) & bmk[tt]);
-                        }
+                        const uint32_t pk = pack_bf2(x0 * gf[2 * p], x1 * gf[2 * p + 1]) & tok[tt];
+                        q[p] = pk | (u4get(gr, p) & gmk[tt]) | (u4get(br, p) & bmk[tt]);
                     }
                 }
                 const uint4 af = make_uint4(q[0], q[1], q[2], q[3]);
@@ -325,7 +309,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
                 for (int j = 0; j < J; ++j)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        rowmaj[(16 * tt + 4 * g + e) * NW + dcol<J, FOLDED>(j, cb)] = acc[tt][j][e];
+                        rowmaj[(16 * tt + 4 * g + e) * NW + J * cb + j] = acc[tt][j][e];
         }
         __syncthreads();
 
@@ -420,7 +404,6 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
                 r = 1.0 / sqrt(sq / (double)d + (double)a.eps);
             }
             sh_r[ss][m] = (float)r;
-            sh_mu[ss][m] = (float)mu;
         }
     }
     __syncthreads();
@@ -437,7 +420,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
         for (int q = 0; q < PPS; ++q) {
             const float* base = a.part + (size_t)pslot[ss][q] * TILE;
             U[ss][q] = 0.f;
-            if (NORM == NORM_LN && !FOLDED && pval[ss][q]) {
+            if (NORM == NORM_LN && pval[ss][q]) {
                 U[ss][q] = base[M * NW + n];
                 add += base[(M + 1) * NW + n];
             }
@@ -447,15 +430,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
                 P[ss][q][i] = (pval[ss][q] && m < M) ? base[m * NW + n] : 0.f;
             }
         }
-    float usum[3] = {0.f, 0.f, 0.f};
-    if (FOLDED) {
-        if (NORM == NORM_LN)
-#pragma unroll
-            for (int ss = 0; ss < 3; ++ss) usum[ss] = a.u[(size_t)ss * d + n0 + n];
-        add += a.c[n0 + n];
-    } else if (a.bias != nullptr) {
-        add += bf_one(a.bias[n0 + n]);
-    }
+    if (a.bias != nullptr) add += bf_one(a.bias[n0 + n]);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int m = rg + RG * i;
@@ -467,10 +442,9 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int q = 0; q < PPS; ++q) {
                 float v = P[ss][q][i];
-                if (NORM == NORM_LN && !FOLDED) v -= sh_delta[(ss * PPS + q) * DECODE_MAX_M + m] * U[ss][q];
+                if (NORM == NORM_LN) v -= sh_delta[(ss * PPS + q) * DECODE_MAX_M + m] * U[ss][q];
                 ys += v;
             }
-            if (FOLDED && NORM == NORM_LN) ys -= sh_mu[ss][m] * usum[ss];
             y += (NORM == NORM_NONE) ? ys : sh_r[ss][m] * ys;
         }
         a.out[(size_t)m * d + n0 + n] = __builtin_bit_cast(uint16_t, (__bf16)(y + add));
@@ -478,9 +452,9 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
     if (tid == 0) a.counters[b] = 0;
 }
 
-DecodePlan plan_decode(int M, int d, int norm, bool folded) {
+DecodePlan plan_decode(int M, int d, int norm) {
     DecodePlan p;
-    const int rows = M + ((norm == NORM_LN && !folded) ? 2 : 0);
+    const int rows = M + (norm == NORM_LN ? 2 : 0);
     p.MT = (rows + 15) / 16;
     p.J = p.MT <= 2 ? 8 : 4;
     if (d % (16 * p.J) != 0) p.J = 4;
@@ -499,36 +473,29 @@ DecodePlan plan_decode(int M, int d, int norm, bool folded) {
     return p;
 }
 
-template <int NORM, int J, int MT, bool FOLDED>
+template <int NORM, int J, int MT>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     const int grid = a.nb * a.kps;
-    decode_kernel<NORM, J, MT, FOLDED><<<grid, DTHREADS, 0, st>>>(a);
+    decode_kernel<NORM, J, MT><<<grid, DTHREADS, 0, st>>>(a);
     return hipGetLastError();
 }
 
-template <int NORM, bool FOLDED>
+template <int NORM>
 static hipError_t launch_decode_n(const DecodeArgs& a, const DecodePlan& p, hipStream_t st) {
     switch (p.MT) {
-        case 1:
-            return p.J == 8 ? launch_decode_t<NORM, 8, 1, FOLDED>(a, st) : launch_decode_t<NORM, 4, 1, FOLDED>(a, st);
-        case 2:
-            return p.J == 8 ? launch_decode_t<NORM, 8, 2, FOLDED>(a, st) : launch_decode_t<NORM, 4, 2, FOLDED>(a, st);
-        case 3: return launch_decode_t<NORM, 4, 3, FOLDED>(a, st);
-        case 4: return launch_decode_t<NORM, 4, 4, FOLDED>(a, st);
-        case 5: return launch_decode_t<NORM, 4, 5, FOLDED>(a, st);
+        case 1: return p.J == 8 ? launch_decode_t<NORM, 8, 1>(a, st) : launch_decode_t<NORM, 4, 1>(a, st);
+        case 2: return p.J == 8 ? launch_decode_t<NORM, 8, 2>(a, st) : launch_decode_t<NORM, 4, 2>(a, st);
+        case 3: return launch_decode_t<NORM, 4, 3>(a, st);
+        case 4: return launch_decode_t<NORM, 4, 4>(a, st);
+        case 5: return launch_decode_t<NORM, 4, 5>(a, st);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <bool FOLDED>
-static hipError_t launch_decode_f(const DecodeArgs& a, int norm, const DecodePlan& p, hipStream_t st) {
-    if (norm == NORM_LN) return launch_decode_n<NORM_LN, FOLDED>(a, p, st);
-    if (norm == NORM_RMS) return launch_decode_n<NORM_RMS, FOLDED>(a, p, st);
-    return launch_decode_n<NORM_NONE, FOLDED>(a, p, st);
-}
-
-hipError_t launch_decode(const DecodeArgs& a, int norm, bool folded, const DecodePlan& p, hipStream_t st) {
-    return folded ? launch_decode_f<true>(a, norm, p, st) : launch_decode_f<false>(a, norm, p, st);
+hipError_t launch_decode(const DecodeArgs& a, int norm, const DecodePlan& p, hipStream_t st) {
+    if (norm == NORM_LN) return launch_decode_n<NORM_LN>(a, p, st);
+    if (norm == NORM_RMS) return launch_decode_n<NORM_RMS>(a, p, st);
+    return launch_decode_n<NORM_NONE>(a, p, st);
 }
 
 }  // namespace e31

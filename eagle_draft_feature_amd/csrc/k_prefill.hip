@@ -1,12 +1,11 @@
 // Prefill path of the fused per-state norm + FC (many tokens): a bf16 MFMA
-// GEMM on the raw hidden states and the folded weight W'^T [d, 3d].
+// GEMM on the raw hidden states and the folded weight W'.
 //
 // With the norm parameters folded into the FC (EAGLE 3.1 explainer,
 // llm-wiki.hwlabs.dev/study/dist/ai-frontier/76.html, section
 // "FC 정규화: EAGLE 3.1의 핵심 수정": the parameters are absorbed by the FC),
 //     out = sum_s rstd_s * (h_s . W'_s^T - mu_s * u_s) + c,
-// so the main loop is a plain NT GEMM (both operands k-contiguous) over the
-// three states in turn, and the normalisation is a per-row rescale of the
+// so the main loop is a plain GEMM over the three states in turn, and the normalisation is a per-row rescale of the
 // accumulator at each state boundary:
 //     acc <- (acc - mu_s * u_s) * rstd_s / rstd_{s+1},
 // finished by acc <- (acc - mu_2 * u_2) * rstd_2 + c.  The statistics come
@@ -14,8 +13,11 @@
 //
 // Tiling for gfx950: 256 x 256 output tile, BK = 64, 512 threads (8 waves as
 // 2 x 4, each wave 128 x 64 = 8 x 4 MFMA 16x16x32 blocks), operand tiles
-// double-buffered in LDS (2 x 64 KiB) with a 16-byte XOR swizzle so the
-// 16 lanes reading one k-chunk of 16 rows hit distinct banks.  Tiles are
+// double-buffered in LDS (2 x 64 KiB).  A (hidden states, row-major) is
+// staged with a 16-byte XOR swizzle so the 16 lanes reading one k-chunk of
+// 16 rows hit distinct banks; W' arrives as 1 KiB MFMA B-fragment tiles
+// (16 columns x 32 k, lane l's operand at bytes [16 l, 16 l + 16)), copied
+// to LDS as they are, so a B operand is one conflict-free 16-byte read.  Tiles are
 // walked in groups of 4 M-tiles, and consecutive workgroup ids are spread so
 // that each XCD (workgroup id mod 8) takes a contiguous run of that order:
 // the 32 tiles an XCD runs at once share A and B tiles in its L2.
@@ -76,8 +78,12 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
         kt1 = s * KTS + ((j + 1) * KTS) / kps;
     }
 
-    // loader role: row lr (+64 i), 16-byte chunk lq of the 128-byte k slice
+    // A loader role: row lr (+64 i), 16-byte chunk lq of the 128-byte k slice.
+    // B loader role: 16-byte piece tid + 512 i of the k-tile's 16 column
+    // blocks x 2 tiles (each column block's two tiles are one 2 KiB run).
     const int lr = tid >> 3, lq = tid & 7;
+    const int T = (int)(K3 / 32);  // tiles per column block
+    const uint4* __restrict__ wt4 = reinterpret_cast<const uint4*>(a.wt);
     uint4 ra[4], rb[4];
     auto gload = [&](int kt) {
         const int s = kt / KTS;
@@ -88,9 +94,10 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
             const int m = m0 + lr + 64 * i;
             ra[i] = make_uint4(0u, 0u, 0u, 0u);
             if (m < M) ra[i] = *reinterpret_cast<const uint4*>(hs + (size_t)m * d + kl);
-            const int n = n0 + lr + 64 * i;
+            const int p = tid + PTH * i;
+            const int nb = (n0 >> 4) + (p >> 7);
             rb[i] = make_uint4(0u, 0u, 0u, 0u);
-            if (n < d) rb[i] = *reinterpret_cast<const uint4*>(a.wt + (size_t)n * K3 + (size_t)kt * PBK + 8 * lq);
+            if (nb < (d >> 4)) rb[i] = wt4[((size_t)nb * T + 2 * kt) * 64 + (p & 127)];
         }
     };
     auto lstore = [&](int stage) {
@@ -100,7 +107,7 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
         for (int i = 0; i < 4; ++i) {
             const int r = lr + 64 * i;
             A[r * 8 + (lq ^ (r & 7))] = ra[i];
-            B[r * 8 + (lq ^ (r & 7))] = rb[i];
+            B[tid + PTH * i] = rb[i];
         }
     };
 
@@ -173,10 +180,7 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
             const int q = 4 * kk + g;
             uint4 bfr[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = wn * 64 + 16 * j + cb;
-                bfr[j] = B[r * 8 + (q ^ (r & 7))];
-            }
+            for (int j = 0; j < 4; ++j) bfr[j] = B[((wn * 4 + j) * 2 + kk) * 64 + lane];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int r = wm * 128 + 16 * i + cb;

@@ -12,15 +12,13 @@ hipError_t launch_row_stats(const uint16_t* h0, const uint16_t* h1, const uint16
                             float eps, float* mu, float* rstd, hipStream_t st);
 
 // ------------------------------------------------------------------- decode
-// Small-M path: one launch, split-K over W in its stored [3d, d] layout.
+// Small-M path on the stored W: one launch, split-K over W in its [3d, d]
+// layout, the norm applied to the A operand (LayerNorm with a shift).
 struct DecodeArgs {
     const uint16_t* h[3];
     const uint16_t* gamma[3];  // NULL entry: gamma = 1
     const uint16_t* beta[3];   // NULL entry: beta = 0
     const uint16_t* W;         // [3d, d] (stored layout)
-    const uint16_t* wt;        // [d, 3d] folded + transposed (folded variant)
-    const float* u;            // [3, d] (folded variant)
-    const float* c;            // [d] (folded variant)
     const uint16_t* bias;      // [d] or NULL
     uint16_t* out;             // [M, d]
     int M, d;
@@ -39,24 +37,45 @@ struct DecodePlan {
 };
 
 constexpr int DECODE_MAX_M = 64;
-DecodePlan plan_decode(int M, int d, int norm, bool folded);
-hipError_t launch_decode(const DecodeArgs& a, int norm, bool folded, const DecodePlan& p, hipStream_t st);
+DecodePlan plan_decode(int M, int d, int norm);
+hipError_t launch_decode(const DecodeArgs& a, int norm, const DecodePlan& p, hipStream_t st);
 
-// Small-M path on the folded weight: one workgroup per 16 columns over the
-// whole K, statistics from the row-statistics pass (no workspace, no atomics).
-struct DecodeColsArgs {
+// ------------------------------------------------------- folded weight tiles
+// The folded weight W' (3d x d, W'[k][n] = bf16(gamma_s[k - s d] W[k][n]))
+// is stored as 1 KiB tiles of 16 columns x 32 k in MFMA B-fragment order:
+// tile (n / 16, k / 32) starts at element ((n / 16) * (3d / 32) + k / 32) * 512,
+// and inside it element (n, k) sits at lane l = 16 * ((k % 32) / 8) + n % 16,
+// position k % 8: offset 8 * l + k % 8.  A 16-column block is one contiguous
+// run of 3d / 32 tiles along k.
+__host__ __device__ inline size_t wtile_index(size_t n, size_t k, size_t d) {
+    return ((n >> 4) * (3 * d / 32) + (k >> 5)) * 512 + ((((k & 31) >> 3) << 4) + (n & 15)) * 8 + (k & 7);
+}
+
+// Small-M path on the folded weight: workgroups of 64 columns x one K chunk
+// (a piece of one state), statistics from the same A fragments, the last
+// workgroup of each column group reduces the chunks.
+struct GemvArgs {
     const uint16_t* h[3];
-    const uint16_t* wt;   // [d, 3d] folded + transposed
+    const uint16_t* wp;   // folded weight tiles
     const float* u;       // [3, d]
     const float* c;       // [d]
-    const float* mu;      // [3, M]
-    const float* rstd;    // [3, M]
     uint16_t* out;        // [M, d]
     int M, d;
     float eps;
-    bool instats;         // statistics in the kernel (M <= 16) instead of mu / rstd
+    int kps;              // K chunks per state (from the plan)
+    int waves;            // waves per workgroup (from the plan)
+    int* counters;        // [d / 64], zero on entry, left zero on exit
+    float* stats;         // [d/64 * 3 kps * 64 * 3]
+    float* part;          // [d/64 * 3 kps * 16 MT * 64]
 };
-hipError_t launch_decode_cols(const DecodeColsArgs& a, int norm, hipStream_t st);
+
+struct GemvPlan {
+    int kps = 0, ring = 0, waves = 0, MT = 1, grid = 0;
+    size_t counters_bytes = 0, stats_bytes = 0, part_bytes = 0;
+};
+
+GemvPlan plan_gemv(int M, int d);
+hipError_t launch_gemv(const GemvArgs& a, int norm, const GemvPlan& p, hipStream_t st);
 
 // -------------------------------------------------------------- fold prepare
 hipError_t launch_fold_prepare(int d, int norm, const uint16_t* const gamma[3], const uint16_t* const beta[3],
@@ -64,11 +83,11 @@ hipError_t launch_fold_prepare(int d, int norm, const uint16_t* const gamma[3], 
                                hipStream_t st);
 
 // ------------------------------------------------------------------ prefill
-// Large-M path: NT GEMM on raw hidden states and the folded, transposed W',
+// Large-M path: GEMM on raw hidden states and the folded weight tiles,
 // per-row rescale at the state boundaries (fold), optional split-K.
 struct PrefillArgs {
     const uint16_t* h[3];
-    const uint16_t* wt;   // [d, 3d] folded + transposed
+    const uint16_t* wt;   // folded weight tiles
     const float* u;       // [3, d]
     const float* c;       // [d]
     const float* mu;      // [3, M]

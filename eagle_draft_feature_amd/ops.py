@@ -118,8 +118,14 @@ def fuse_ws(h_low, h_mid, h_high, norm, eps, gammas, betas, W, bias, workspace: 
     return out
 
 
+def folded_shape(d: int):
+    """Shape given to the folded weight: [d/16, 3d/32, 64, 8] bf16, i.e. column
+    block, k-step of 32, MFMA lane, 8 consecutive k (1 KiB per tile)."""
+    return (d // 16, 3 * d // 32, 64, 8)
+
+
 def fold_prepare(norm: Union[int, str], gammas, betas, W: torch.Tensor, bias: Optional[torch.Tensor]):
-    """eagle31_fold_prepare: returns (w_folded [d, 3d] bf16, u [3, d] f32, c [d] f32)."""
+    """eagle31_fold_prepare: returns (w_folded bf16 tiles, u [3, d] f32, c [d] f32)."""
     _want(W, "W")
     if W.dim() != 2 or W.shape[0] != 3 * W.shape[1]:
         raise ValueError("W must be [3d, d]")
@@ -127,7 +133,7 @@ def fold_prepare(norm: Union[int, str], gammas, betas, W: torch.Tensor, bias: Op
     dev = W.device
     if bias is not None:
         _want(bias, "bias", shape=(d,), device=dev)
-    wf = torch.empty((d, 3 * d), dtype=torch.bfloat16, device=dev)
+    wf = torch.empty(folded_shape(d), dtype=torch.bfloat16, device=dev)
     u = torch.empty((3, d), dtype=torch.float32, device=dev)
     c = torch.empty((d,), dtype=torch.float32, device=dev)
     g = _vec3(gammas, "gammas", d, dev)
@@ -142,7 +148,7 @@ def fuse_folded(h_low, h_mid, h_high, norm, eps, w_folded: torch.Tensor, u: torc
                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """eagle31_fuse_folded (or _ws when a workspace is given) on prepared weights."""
     M, d, dev = _states(h_low, h_mid, h_high)
-    _want(w_folded, "w_folded", shape=(d, 3 * d), device=dev)
+    _want(w_folded, "w_folded", shape=folded_shape(d), device=dev)
     _want(u, "u", dtype=torch.float32, shape=(3, d), device=dev)
     _want(c, "c", dtype=torch.float32, shape=(d,), device=dev)
     if out is None:

@@ -120,15 +120,22 @@ int eagle31_fuse_ws(const void* h_low, const void* h_mid, const void* h_high, in
  * the LayerNorm parameters are taken into the FC layer, no weights are added).
  *
  * Outputs (caller-owned device memory):
- *   w_folded  bf16 [d, 3d], the TRANSPOSED scaled weight: element (n, k) at
- *             n*3d + k equals bf16_rne(gamma_s[k - s*d] * W[k, n]) for
- *             LAYERNORM / RMSNORM and W[k, n] for NONE;
- *   u         float32 [3, d]: u[s][n] = sum over k in state s of w_folded(n, k)
+ *   w_folded  bf16, 3*d*d elements: W'[k, n] = bf16_rne(gamma_s[k - s*d] * W[k, n])
+ *             for LAYERNORM / RMSNORM and W[k, n] for NONE (s = k / d), stored
+ *             as 1 KiB tiles of 16 columns x 32 k in the operand order of the
+ *             gfx950 16x16x32 bf16 matrix instruction:
+ *                 tile (n / 16, k / 32) starts at element
+ *                     ((n / 16) * (3d / 32) + k / 32) * 512,
+ *                 and holds W'[k, n] at offset 8 * (16 * ((k % 32) / 8) + n % 16) + k % 8
+ *             (the 16 bytes of lane l = 16 * ((k % 32) / 8) + n % 16 are 8
+ *             consecutive k of one column; the tiles of a 16-column block
+ *             are consecutive along k, so that block is one contiguous run);
+ *   u         float32 [3, d]: u[s][n] = sum over k in state s of W'[k, n]
  *             (from the stored, rounded values; unused by NONE);
  *   c         float32 [d]: c[n] = bias[n] + sum_s sum_k beta_s[k] W[s*d + k, n]
  *             (the beta term for LAYERNORM only).
  * Then, for the same norm_kind,
- *   out = sum_s rstd_s * (h_s . w_folded_s^T - mu_s * u_s) + c
+ *   out = sum_s rstd_s * (h_s . W'_s - mu_s * u_s) + c
  * equals eagle31_fuse's result up to rounding.
  */
 int eagle31_fold_prepare(int64_t d, int norm_kind, const void* const* gamma, const void* const* beta,

@@ -24,6 +24,13 @@ def to_dev(bits: np.ndarray, device="cuda"):
     return t.to(device)
 
 
+def unpack_folded(tiles, d: int) -> np.ndarray:
+    """The folded weight's tiles back to W' [3d, d], from the layout the C
+    header documents: tile (n/16, k/32), lane 16*((k%32)/8) + n%16, slot k%8."""
+    t = np.asarray(tiles).reshape(d // 16, 3 * d // 32, 4, 16, 8)  # nb, kstep, kgroup, ncol, kk
+    return np.transpose(t, (1, 2, 4, 0, 3)).reshape(3 * d, d)
+
+
 def bf16_to_f64(t) -> np.ndarray:
     """Device bf16 tensor -> float64 numpy (exact)."""
     import torch

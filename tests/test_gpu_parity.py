@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from parity import DevInputs, assert_parity, bf16_to_f64, sample_rows, to_dev
+from parity import DevInputs, assert_parity, bf16_to_f64, sample_rows, to_dev, unpack_folded
 
 pytestmark = pytest.mark.gpu
 
@@ -151,7 +151,7 @@ def test_fold_prepare_exact_weight_and_vectors(cfg, kind, eps):
     b = None if inp.beta is None else [oracle.decode_bf16(x) for x in inp.beta]
     bias = None if inp.bias is None else oracle.decode_bf16(inp.bias)
     Wf, uo, co = oracle.fold_prepare(kind, g, b, W, bias, round_w=oracle.round_bf16_rne)
-    got = bf16_to_f64(wf).T
+    got = unpack_folded(bf16_to_f64(wf), inp.d)
     assert np.array_equal(got, Wf), f"W' mismatch in {np.sum(got != Wf)} elements"
     uo_scale = np.abs(Wf).sum() / Wf.shape[1] / 3
     assert np.max(np.abs(u.cpu().numpy() - uo)) <= 1e-5 * max(uo_scale, 1.0)
@@ -244,6 +244,22 @@ def test_edge_shapes(d, M, kind):
     eps = 1e-5
     G = run_fuse(dv, kind, eps)
     assert_parity(G, oracle_rows(inp, kind, eps), f"edge d={d} M={M}")
+
+
+@pytest.mark.parametrize("d,M,kind", [(64, 1, LN), (64, 3, RMS), (192, 17, LN), (320, 33, RMS), (512, 64, NONE),
+                                      (1024, 40, LN), (4160, 5, LN), (5120, 64, RMS)])
+def test_folded_edge_shapes(d, M, kind):
+    """The folded decode kernel at widths that change its plan (waves per
+    workgroup, chunks per state, ring depth) and ragged token counts."""
+    note(f"folded edge d={d} M={M} kind={kind}")
+    w = synth.gen.custom_workload(d, (M,), seed_tag=d * 11 + M)
+    inp = synth.make_inputs(w, M)
+    dv = DevInputs(inp)
+    eps = 1e-5
+    wf, u, c = e31().fold_prepare(kind, dv.gamma, dv.beta, dv.W, dv.bias)
+    out = e31().fuse_folded(dv.h[0], dv.h[1], dv.h[2], kind, eps, wf, u, c)
+    torch.cuda.synchronize()
+    assert_parity(bf16_to_f64(out), oracle_rows(inp, kind, eps), f"folded edge d={d} M={M}")
 
 
 def test_optional_parameters_absent():
