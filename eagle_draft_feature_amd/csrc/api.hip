@@ -6,6 +6,7 @@
 // split-K with in-kernel statistics); larger M runs the row-statistics pass and the folded GEMM,
 // preparing W', u and c into the workspace first when the caller passed the
 // stored W.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -92,9 +93,9 @@ WsLayout layout_for(int64_t M, int64_t d, int norm, bool folded) {
     L.counters_bytes = COUNTER_REGION;
     size_t off = COUNTER_REGION;
     if (M <= DECODE_MAX_M && folded) {
-        const GemvPlan p = plan_gemv((int)M, (int)d);
+        const GemvPlan p = plan_gemv((int)M, (int)d, norm);
         L.stats = off;
-        off += up256(p.stats_bytes);
+        off += up256(GemvPlan::rstats_bytes);
         L.part = off;
         off += up256(p.part_bytes);
         L.total = off;
@@ -169,6 +170,18 @@ int owned_workspace(size_t need, hipStream_t st, void** out_ptr, size_t* out_byt
     return EAGLE31_OK;
 }
 
+// Id stamped on the statistics records of one decode call: process-wide,
+// never 0 (a zeroed workspace holds no valid record), so a record left by an
+// earlier call on the same workspace never matches.
+uint32_t next_call_id() {
+    static std::atomic<uint32_t> counter{0};
+    uint32_t id;
+    do {
+        id = counter.fetch_add(1, std::memory_order_relaxed) + 1;
+    } while (id == 0);
+    return id;
+}
+
 template <typename T>
 T* at(void* base, size_t off) {
     return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
@@ -191,8 +204,8 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
 
     hipError_t e;
     if (M <= DECODE_MAX_M && folded) {
-        const GemvPlan p = plan_gemv((int)M, (int)d);
-        if (p.kps == 0 || d / 64 > MAX_COUNTERS) return EAGLE31_ERR_SHAPE;
+        const GemvPlan p = plan_gemv((int)M, (int)d, norm);
+        if (p.waves == 0 || (p.kind == GEMV_SPLIT && d / 64 > MAX_COUNTERS)) return EAGLE31_ERR_SHAPE;
         GemvArgs a;
         for (int s = 0; s < 3; ++s) a.h[s] = h[s];
         a.wp = static_cast<const uint16_t*>(wt);
@@ -204,9 +217,11 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
         a.eps = eps;
         a.kps = p.kps;
         a.waves = p.waves;
+        a.stat_waves = p.stat_waves;
         a.counters = at<int>(ws, L.counters);
-        a.stats = at<float>(ws, L.stats);
         a.part = at<float>(ws, L.part);
+        a.rstats = at<uint32_t>(ws, L.stats);
+        a.call_id = next_call_id();
         e = launch_gemv(a, norm, p, st);
         if (e != hipSuccess) return hip_fail(e);
         return EAGLE31_OK;

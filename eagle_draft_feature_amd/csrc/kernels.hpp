@@ -51,9 +51,11 @@ __host__ __device__ inline size_t wtile_index(size_t n, size_t k, size_t d) {
     return ((n >> 4) * (3 * d / 32) + (k >> 5)) * 512 + ((((k & 31) >> 3) << 4) + (n & 15)) * 8 + (k & 7);
 }
 
-// Small-M path on the folded weight: workgroups of 64 columns x one K chunk
-// (a piece of one state), statistics from the same A fragments, the last
-// workgroup of each column group reduces the chunks.
+// Small-M path on the folded weight.  M <= 8: one workgroup per 16
+// columns over the whole K (no workspace).  M > 8: workgroups of 64
+// columns x one K chunk (a piece of one state), the last workgroup of each
+// column group reduces the chunks through the workspace.  Statistics come
+// from the A fragments in both.
 struct GemvArgs {
     const uint16_t* h[3];
     const uint16_t* wp;   // folded weight tiles
@@ -62,19 +64,27 @@ struct GemvArgs {
     uint16_t* out;        // [M, d]
     int M, d;
     float eps;
-    int kps;              // K chunks per state (from the plan)
-    int waves;            // waves per workgroup (from the plan)
-    int* counters;        // [d / 64], zero on entry, left zero on exit
-    float* stats;         // [d/64 * 3 kps * 64 * 3]
-    float* part;          // [d/64 * 3 kps * 16 MT * 64]
+    int kps;              // K chunks per state (split plan)
+    int waves;            // streaming waves per workgroup (from the plan)
+    int stat_waves;       // statistics waves per workgroup (cols plan)
+    int* counters;        // [d / 64], zero on entry, left zero on exit (split)
+    float* part;          // [d/64 * 3 kps * 16 MT * 64] (split)
+    uint32_t* rstats;     // [3 M][4]: (K, S1, S2, call id) per (state, token) row
+    uint32_t call_id;     // nonzero, different from the previous calls' on this workspace
 };
+
+constexpr int GEMV_COLS_MAX_M = 8;  // above this the split kernel reads A 4x less often
+constexpr int GEMV_COLS = 0;
+constexpr int GEMV_SPLIT = 1;
 
 struct GemvPlan {
-    int kps = 0, ring = 0, waves = 0, MT = 1, grid = 0;
-    size_t counters_bytes = 0, stats_bytes = 0, part_bytes = 0;
+    int kind = GEMV_COLS;
+    int kps = 0, ring = 0, waves = 0, stat_waves = 0, MT = 1, grid = 0;
+    size_t counters_bytes = 0, part_bytes = 0;
+    static constexpr size_t rstats_bytes = 3 * 64 * 4 * sizeof(uint32_t);
 };
 
-GemvPlan plan_gemv(int M, int d);
+GemvPlan plan_gemv(int M, int d, int norm);
 hipError_t launch_gemv(const GemvArgs& a, int norm, const GemvPlan& p, hipStream_t st);
 
 // -------------------------------------------------------------- fold prepare
