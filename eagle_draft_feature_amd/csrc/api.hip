@@ -3,7 +3,7 @@
 // Every argument check runs on the host before the first HIP call; a failed
 // check enqueues nothing.  Dispatch: M <= 64 runs a single-launch decode
 // kernel, on W in its stored layout or on the folded weight tiles (both
-// split-K with in-kernel statistics); larger M runs the row-statistics pass and the folded GEMM,
+// split-K, statistics inside the launch); larger M runs the row-statistics pass and the folded GEMM,
 // preparing W', u and c into the workspace first when the caller passed the
 // stored W.
 #include <atomic>
@@ -205,7 +205,7 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
     hipError_t e;
     if (M <= DECODE_MAX_M && folded) {
         const GemvPlan p = plan_gemv((int)M, (int)d, norm);
-        if (p.waves == 0 || (p.kind == GEMV_SPLIT && d / 64 > MAX_COUNTERS)) return EAGLE31_ERR_SHAPE;
+        if (p.waves == 0 || d / (16 * p.nb) > MAX_COUNTERS) return EAGLE31_ERR_SHAPE;
         GemvArgs a;
         for (int s = 0; s < 3; ++s) a.h[s] = h[s];
         a.wp = static_cast<const uint16_t*>(wt);
@@ -217,7 +217,6 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
         a.eps = eps;
         a.kps = p.kps;
         a.waves = p.waves;
-        a.stat_waves = p.stat_waves;
         a.counters = at<int>(ws, L.counters);
         a.part = at<float>(ws, L.part);
         a.rstats = at<uint32_t>(ws, L.stats);

@@ -51,11 +51,10 @@ __host__ __device__ inline size_t wtile_index(size_t n, size_t k, size_t d) {
     return ((n >> 4) * (3 * d / 32) + (k >> 5)) * 512 + ((((k & 31) >> 3) << 4) + (n & 15)) * 8 + (k & 7);
 }
 
-// Small-M path on the folded weight.  M <= 8: one workgroup per 16
-// columns over the whole K (no workspace).  M > 8: workgroups of 64
-// columns x one K chunk (a piece of one state), the last workgroup of each
-// column group reduces the chunks through the workspace.  Statistics come
-// from the A fragments in both.
+// Small-M path on the folded weight: workgroups of 64 or 128 columns x one K chunk
+// (a piece of one state); the last workgroup of each column group reduces
+// the chunks through the workspace.  Row statistics are reduced once per
+// call and handed over as records stamped with the call id.
 struct GemvArgs {
     const uint16_t* h[3];
     const uint16_t* wp;   // folded weight tiles
@@ -64,22 +63,16 @@ struct GemvArgs {
     uint16_t* out;        // [M, d]
     int M, d;
     float eps;
-    int kps;              // K chunks per state (split plan)
-    int waves;            // streaming waves per workgroup (from the plan)
-    int stat_waves;       // statistics waves per workgroup (cols plan)
-    int* counters;        // [d / 64], zero on entry, left zero on exit (split)
-    float* part;          // [d/64 * 3 kps * 16 MT * 64] (split)
+    int kps;              // K chunks per state (from the plan)
+    int waves;            // waves per workgroup (from the plan)
+    int* counters;        // [column groups], zero on entry, left zero on exit
+    float* part;          // [column groups * 3 kps * 16 MT * 16 nb]
     uint32_t* rstats;     // [3 M][4]: (K, S1, S2, call id) per (state, token) row
     uint32_t call_id;     // nonzero, different from the previous calls' on this workspace
 };
 
-constexpr int GEMV_COLS_MAX_M = 8;  // above this the split kernel reads A 4x less often
-constexpr int GEMV_COLS = 0;
-constexpr int GEMV_SPLIT = 1;
-
 struct GemvPlan {
-    int kind = GEMV_COLS;
-    int kps = 0, ring = 0, waves = 0, stat_waves = 0, MT = 1, grid = 0;
+    int kps = 0, ring = 0, waves = 0, nb = 4, MT = 1, grid = 0;  // nb: 16-column blocks per workgroup
     size_t counters_bytes = 0, part_bytes = 0;
     static constexpr size_t rstats_bytes = 3 * 64 * 4 * sizeof(uint32_t);
 };
