@@ -37,11 +37,12 @@
 //    extra pass over the hidden states is made.
 //  * The 8 waves of a workgroup sum their tiles pairwise in LDS in a fixed
 //    order; the workgroup writes a compact row-major partial and its piece
-//    statistics to the workspace.  The last workgroup of a column block to
-//    arrive (atomic counter) combines the statistics (exact shifted-sum
-//    algebra in float64), issues every partial load of its outputs at once,
-//    sums the pieces in a fixed order and resets the counter: the result is
-//    bitwise reproducible and the workspace is ready for the next call.
+//    statistics to the workspace with device-coherent stores.  The last
+//    workgroup of a column block to arrive (atomic counter) combines the
+//    statistics (exact shifted-sum algebra in float64), issues every
+//    partial load of its outputs at once, sums the pieces in a fixed order
+//    and resets the counter: the result is bitwise reproducible and the
+//    workspace is ready for the next call.
 #include <type_traits>
 
 #include "common.hpp"
@@ -314,9 +315,8 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
         __syncthreads();
 
         const int slot = (b * ks + c) * DECODE_SLOTS + pi;
-        float4* part = reinterpret_cast<float4*>(a.part + (size_t)slot * TILE);
-        const float4* src4 = reinterpret_cast<const float4*>(rowmaj);
-        for (int v = tid; v < Mst * NW / 4; v += DTHREADS) part[v] = src4[v];
+        float* part = a.part + (size_t)slot * TILE;
+        for (int v = tid; v < Mst * NW; v += DTHREADS) store_coherent(part + v, rowmaj[v]);
         if (NORM != NORM_NONE) {
             float* st = a.stats + (size_t)slot * DECODE_MAX_M * 3;
             for (int m = tid; m < M; m += DTHREADS) {
@@ -324,28 +324,28 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
                                  ((sh_s1[1][m] + sh_s1[5][m]) + (sh_s1[3][m] + sh_s1[7][m]));
                 const float v2 = ((sh_s2[0][m] + sh_s2[4][m]) + (sh_s2[2][m] + sh_s2[6][m])) +
                                  ((sh_s2[1][m] + sh_s2[5][m]) + (sh_s2[3][m] + sh_s2[7][m]));
-                st[3 * m + 0] = NORM == NORM_LN ? sh_shift[m] : 0.f;
-                st[3 * m + 1] = v1;
-                st[3 * m + 2] = v2;
+                store_coherent(st + 3 * m + 0, NORM == NORM_LN ? sh_shift[m] : 0.f);
+                store_coherent(st + 3 * m + 1, v1);
+                store_coherent(st + 3 * m + 2, v2);
             }
         }
         __syncthreads();  // LDS is reused by the next piece
     }
 
-    // Publish: every wave waits until its own stores have reached L2 (the
-    // workgroup barrier alone does not wait for them), then thread 0's
-    // counter increment is a release at agent scope: one L2 write-back per
-    // workgroup.  Only the last arriver acquires (one L2 invalidate per
-    // column block) before reading the other workgroups' tiles.
+    // Publish without cache maintenance: partials and statistics were
+    // written with device-coherent (agent-scope atomic) stores; every wave
+    // waits until they have completed (the workgroup barrier alone does not
+    // wait for them), then thread 0 counts the workgroup in.  The last
+    // arriver reads them with device-coherent loads.  (An agent-scope
+    // release / acquire would write back / invalidate a whole L2.)
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(a.counters + b, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const int old = __hip_atomic_fetch_add(a.counters + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         sh_last = (old == ks - 1);
     }
     __syncthreads();
     if (!sh_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
     // ================= last arriver of column block b =================
     // Pieces of this column block by state: state s is covered by chunks
@@ -378,9 +378,9 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
                 K[q] = s1[q] = s2[q] = 0.f;
                 if (NORM != NORM_NONE && pval[ss][q]) {
                     const float* st = a.stats + ((size_t)pslot[ss][q] * DECODE_MAX_M + m) * 3;
-                    K[q] = st[0];
-                    s1[q] = st[1];
-                    s2[q] = st[2];
+                    K[q] = load_coherent(st);
+                    s1[q] = load_coherent(st + 1);
+                    s2[q] = load_coherent(st + 2);
                 }
             }
             double r = 1.0, mu = 0.0;
@@ -421,13 +421,13 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
             const float* base = a.part + (size_t)pslot[ss][q] * TILE;
             U[ss][q] = 0.f;
             if (NORM == NORM_LN && pval[ss][q]) {
-                U[ss][q] = base[M * NW + n];
-                add += base[(M + 1) * NW + n];
+                U[ss][q] = load_coherent(base + M * NW + n);
+                add += load_coherent(base + (M + 1) * NW + n);
             }
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const int m = rg + RG * i;
-                P[ss][q][i] = (pval[ss][q] && m < M) ? base[m * NW + n] : 0.f;
+                P[ss][q][i] = (pval[ss][q] && m < M) ? load_coherent(base + m * NW + n) : 0.f;
             }
         }
     if (a.bias != nullptr) add += bf_one(a.bias[n0 + n]);
@@ -449,7 +449,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
         }
         a.out[(size_t)m * d + n0 + n] = __builtin_bit_cast(uint16_t, (__bf16)(y + add));
     }
-    if (tid == 0) a.counters[b] = 0;
+    if (tid == 0) __hip_atomic_store(a.counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 DecodePlan plan_decode(int M, int d, int norm) {
