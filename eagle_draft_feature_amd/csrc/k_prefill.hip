@@ -11,16 +11,20 @@
 // finished by acc <- (acc - mu_2 * u_2) * rstd_2 + c.  The statistics come
 // from the row-statistics pass that runs first.
 //
-// Tiling for gfx950: 256 x 256 output tile, BK = 64, 512 threads (8 waves as
-// 2 x 4, each wave 128 x 64 = 8 x 4 MFMA 16x16x32 blocks), operand tiles
-// double-buffered in LDS (2 x 64 KiB).  A (hidden states, row-major) is
-// staged with a 16-byte XOR swizzle so the 16 lanes reading one k-chunk of
-// 16 rows hit distinct banks; W' arrives as 1 KiB MFMA B-fragment tiles
-// (16 columns x 32 k, lane l's operand at bytes [16 l, 16 l + 16)), copied
-// to LDS as they are, so a B operand is one conflict-free 16-byte read.  Tiles are
-// walked in groups of 4 M-tiles, and consecutive workgroup ids are spread so
-// that each XCD (workgroup id mod 8) takes a contiguous run of that order:
-// the 32 tiles an XCD runs at once share A and B tiles in its L2.
+// Tiling for gfx950: 256 x 256 output tile, BK = 64, 256 threads (4 waves
+// as 2 x 2, each wave 128 x 128 = 8 x 8 MFMA 16x16x32 blocks, whose 256
+// accumulator registers the compiler keeps in AGPRs).  Operands go from
+// global memory straight to LDS (16-byte LDS-DMA loads, no register
+// staging), double-buffered: the loads of k-tile t+1 are issued before the
+// MFMAs of k-tile t.  A (hidden states, row-major) lands 8 rows x 128 bytes
+// per wave load; its 16-byte chunks are XOR-swizzled by (row / 2) mod 8 on
+// the global side, so the 16 rows of a fragment read hit distinct banks.
+// W' arrives as 1 KiB MFMA B-fragment tiles (16 columns x 32 k, lane l's
+// operand at bytes [16 l, 16 l + 16)), copied to LDS as they are, so a B
+// operand is one conflict-free 16-byte read.  Tiles are walked in groups
+// of 4 M-tiles, and consecutive workgroup ids are spread so that each XCD
+// (workgroup id mod 8) takes a contiguous run of that order: the tiles an
+// XCD runs at once share A and B tiles in its L2.
 // Few tiles (small M) split K by chunks that never cross a state; partials go
 // to a workspace and the last workgroup of a tile sums them in a fixed order.
 #include "common.hpp"
@@ -28,9 +32,13 @@
 
 namespace e31 {
 
-constexpr int PBM = 256, PBN = 256, PBK = 64, PTH = 512;
+constexpr int PBM = 256, PBN = 256, PBK = 64, PTH = 256;
 constexpr int PGM = 4;  // M-tiles per raster group
-constexpr int STAGE_U4 = (PBM + PBN) * PBK / 8;  // uint4 per LDS stage (A then B)
+constexpr int PFD = 3;  // L2 prefetch distance in k-tiles
+// s_waitcnt immediate: vmcnt <= 2, lgkmcnt = 0, expcnt not waited for
+constexpr int WAIT_VM2 = 2 | (7 << 4) | (0 << 8);
+constexpr int STAGE_A = PBM * PBK * 2;           // bytes of an A stage (32 KiB)
+constexpr int STAGE_BYTES = (PBM + PBN) * PBK * 2;  // A then B (64 KiB)
 
 struct TileCoord {
     int mt, nt, chunk;
@@ -56,7 +64,10 @@ __device__ __forceinline__ TileCoord map_tile(int bid, int TM, int TN, int split
 
 template <bool SPLIT, int NORM>
 __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, int TN) {
-    __shared__ __attribute__((aligned(16))) uint4 lds[2 * STAGE_U4];
+    // two stages in separate arrays: with static stage indices the compiler
+    // can tell the LDS-DMA writes of one stage from the reads of the other
+    __shared__ __attribute__((aligned(1024))) char stage0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char stage1[STAGE_BYTES];
     // per-row factors of the tile: mu_0, rstd_0/rstd_1, mu_1, rstd_1/rstd_2, mu_2, rstd_2
     // per-column factors: u_0, u_1, u_2, c
     __shared__ float rowf[6][PBM];
@@ -67,8 +78,9 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
     const int M = a.M, d = a.d;
     const size_t K3 = (size_t)3 * d;
     const int m0 = tc.mt * PBM, n0 = tc.nt * PBN;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, cb = lane & 15;
-    const int wm = wave >> 2, wn = wave & 3;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, cb = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave bases stay scalar
+    const int wm = wave >> 1, wn = wave & 1;
     const int KTS = d / PBK;  // k-tiles per state
     int kt0 = 0, kt1 = 3 * KTS;
     if (SPLIT) {
@@ -78,45 +90,77 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
         kt1 = s * KTS + ((j + 1) * KTS) / kps;
     }
 
-    // A loader role: row lr (+64 i), 16-byte chunk lq of the 128-byte k slice.
-    // B loader role: 16-byte piece tid + 512 i of the k-tile's 16 column
-    // blocks x 2 tiles (each column block's two tiles are one 2 KiB run).
-    const int lr = tid >> 3, lq = tid & 7;
+    // Loader roles (per stage, 32 A blocks and 32 B tiles of 1 KiB; wave w
+    // issues A blocks and B tiles 8 w .. 8 w + 7):
+    //  A block ab: rows 8 ab + lane / 8, LDS chunk lane % 8 holds global
+    //  chunk (lane % 8) ^ ((row / 2) % 8); rows past M re-read row M - 1.
+    //  B tile bt: column block n0 / 16 + bt / 2 (clamped), k-step 2 kt + bt % 2.
+    // Addresses are a wave-uniform base plus a 32-bit per-lane byte offset.
     const int T = (int)(K3 / 32);  // tiles per column block
-    const uint4* __restrict__ wt4 = reinterpret_cast<const uint4*>(a.wt);
-    uint4 ra[4], rb[4];
-    auto gload = [&](int kt) {
+    const int nblk = d >> 4;
+    uint32_t aoff[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int r = 8 * (8 * wave + q) + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        aoff[q] = (uint32_t)((min(m0 + r, M - 1) - m0) * d + 8 * c) * 2u;  // < 512 d bytes
+    }
+    const char* wbase = reinterpret_cast<const char*>(a.wt);
+    const uint32_t boff = (uint32_t)lane * 16u;
+    auto issue = [&](int kt, char* sa) __attribute__((always_inline)) {
         const int s = kt / KTS;
-        const int kl = kt * PBK - s * d + 8 * lq;
-        const uint16_t* hs = a.h[s];
+        const char* hs = reinterpret_cast<const char*>((s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2])) +
+                                                       (size_t)m0 * d + (kt * PBK - s * d));
+        char* sb = sa + STAGE_A;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = m0 + lr + 64 * i;
-            ra[i] = make_uint4(0u, 0u, 0u, 0u);
-            if (m < M) ra[i] = *reinterpret_cast<const uint4*>(hs + (size_t)m * d + kl);
-            const int p = tid + PTH * i;
-            const int nb = (n0 >> 4) + (p >> 7);
-            rb[i] = make_uint4(0u, 0u, 0u, 0u);
-            if (nb < (d >> 4)) rb[i] = wt4[((size_t)nb * T + 2 * kt) * 64 + (p & 127)];
-        }
-    };
-    auto lstore = [&](int stage) {
-        uint4* A = lds + stage * STAGE_U4;
-        uint4* B = A + PBM * PBK / 8;
+        for (int q = 0; q < 8; ++q)
+            __builtin_amdgcn_global_load_lds(hs + aoff[q], sa + (8 * wave + q) * 1024, 16, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = lr + 64 * i;
-            A[r * 8 + (lq ^ (r & 7))] = ra[i];
-            B[tid + PTH * i] = rb[i];
+        for (int q = 0; q < 8; ++q) {
+            const int bt = 8 * wave + q;
+            const int nb = min((n0 >> 4) + (bt >> 1), nblk - 1);
+            const char* src = wbase + (((size_t)nb * T + 2 * kt + (bt & 1)) << 10);
+            __builtin_amdgcn_global_load_lds(src + boff, sb + bt * 1024, 16, 0, 0);
         }
     };
 
-    f32x4 acc[8][4];
+    // L2 prefetch of k-tile kt + PFD: every CU of an XCD asks for the same new
+    // k-slice at about the same time, so without it each k-tile pays the
+    // latency of memory, which one stage of lookahead cannot hide.  Thread t
+    // touches one dword of A row t and of B line t (16 lines of 128 bytes per
+    // column block): the whole k-slice of the tile.  The loaded words are
+    // kept until the next k-tile so that the wait at the end of a k-tile can
+    // leave the newest prefetch in flight.
+    const uint32_t pf_aoff = (uint32_t)(min(m0 + tid, M - 1) - m0) * (uint32_t)d * 2u;
+    const char* pf_b = wbase + ((size_t)min((n0 >> 4) + (tid >> 4), nblk - 1) * T << 10) + (tid & 15) * 128;
+    uint32_t pf_keep0 = 0, pf_keep1 = 0;
+    auto prefetch = [&](int kt, uint32_t& w0, uint32_t& w1) __attribute__((always_inline)) {
+        const int kp = min(kt + PFD, kt1 - 1);
+        const int s = kp / KTS;
+        const char* hs = reinterpret_cast<const char*>((s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2])) +
+                                                       (size_t)m0 * d + (kp * PBK - s * d));
+        w0 = __hip_atomic_load(reinterpret_cast<const uint32_t*>(hs + pf_aoff), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+        w1 = __hip_atomic_load(reinterpret_cast<const uint32_t*>(pf_b + ((size_t)kp << 11)), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    };
+
+    // fragment reads: A row wm 128 + 16 i + lane % 16, chunk 4 kk + lane / 16;
+    // the swizzle (row / 2) % 8 is the same for the 8 row blocks, so one base
+    // per kk and an immediate offset of 2048 i bytes
+    uint32_t aread[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int r = wm * 128 + cb;
+        aread[kk] = (uint32_t)(r * 128 + 16 * ((4 * kk + g) ^ ((r >> 1) & 7)));
+    }
+    const uint32_t bread = (uint32_t)(STAGE_A + wn * 16384) + (uint32_t)lane * 16u;
+
+    f32x4 acc[8][8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (tid < PBM) {
         const int m = m0 + tid;
@@ -134,28 +178,26 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
         }
 #pragma unroll
         for (int q = 0; q < 6; ++q) rowf[q][tid] = f[q];
-    } else if (tid < PBM + PBN) {
-        const int cl = tid - PBM;
-        const int n = n0 + cl;
-        float f[4] = {0.f, 0.f, 0.f, 0.f};
+        const int n = n0 + tid;
+        float h4[4] = {0.f, 0.f, 0.f, 0.f};
         if (n < d) {
             if (NORM == NORM_LN) {
-                f[0] = a.u[n];
-                f[1] = a.u[(size_t)d + n];
-                f[2] = a.u[(size_t)2 * d + n];
+                h4[0] = a.u[n];
+                h4[1] = a.u[(size_t)d + n];
+                h4[2] = a.u[(size_t)2 * d + n];
             }
-            f[3] = a.c[n];
+            h4[3] = a.c[n];
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) colf[q][cl] = f[q];
+        for (int q = 0; q < 4; ++q) colf[q][tid] = h4[q];
     }
-    // (visible to all after the first barrier of the main loop)
+    // (visible to all after the first barrier below)
 
     // acc <- (acc - mu_s u_s) * factor_s, per row (factor: rstd ratio, or rstd_2 at the end)
-    auto rescale = [&](int s) {
-        float uc[4];
+    auto rescale = [&](int s) __attribute__((always_inline)) {
+        float uc[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) uc[j] = colf[s][wn * 64 + 16 * j + cb];
+        for (int j = 0; j < 8; ++j) uc[j] = colf[s][wn * 128 + 16 * j + cb];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
 #pragma unroll
@@ -163,58 +205,83 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
                 const int r = wm * 128 + 16 * i + 4 * g + e;
                 const float mu = rowf[2 * s][r], fac = rowf[2 * s + 1][r];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j][e] = (acc[i][j][e] - mu * uc[j]) * fac;
+                for (int j = 0; j < 8; ++j) acc[i][j][e] = (acc[i][j][e] - mu * uc[j]) * fac;
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    auto body = [&](int kt) {
-        const int stage = (kt - kt0) & 1;
-        const bool more = kt + 1 < kt1;
-        if (more) gload(kt + 1);
-        const uint4* A = lds + stage * STAGE_U4;
-        const uint4* B = A + PBM * PBK / 8;
+    // all 32 fragment reads of the k-tile first (128 VGPRs), then the 128 MFMAs,
+    // so the LDS latency is paid once per k-tile rather than per row block
+    // all 32 fragment reads of the k-tile first (128 VGPRs), then the 128 MFMAs,
+    // so the LDS latency is paid once per k-tile rather than per row block
+    auto compute = [&](const char* sa) __attribute__((always_inline)) {
+        u32x4 bfr[2][8], af[2][8];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            const int q = 4 * kk + g;
-            uint4 bfr[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bfr[j] = B[((wn * 4 + j) * 2 + kk) * 64 + lane];
+            for (int j = 0; j < 8; ++j)
+                bfr[kk][j] = *reinterpret_cast<const u32x4*>(sa + bread + (2 * j + kk) * 1024);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int r = wm * 128 + 16 * i + cb;
-                const uint4 af = A[r * 8 + (q ^ (r & 7))];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = mfma16x16x32(af, bfr[j], acc[i][j]);
-            }
+            for (int i = 0; i < 8; ++i) af[kk][i] = *reinterpret_cast<const u32x4*>(sa + aread[kk] + 2048 * i);
         }
-        if (more) lstore(stage ^ 1);
-        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = mfma16x16x32(af[kk][i], bfr[kk][j], acc[i][j]);
     };
 
-    gload(kt0);
-    lstore(0);
-    __syncthreads();
-    // one loop per state so the boundary rescale stays out of the hot loop
+    // k-tile kt of a state ending at kb: load kt + 1 into the other stage, MFMAs
+    // on this one, then wait for that load and for every wave to be done with
+    // this stage.  The barrier is a bare s_barrier: a fence would also wait for
+    // the L2 prefetch still in flight.
+    auto step = [&](int kt, int kb, char* cur, char* nxt) __attribute__((always_inline)) {
+        if (kt + 1 < kb) issue(kt + 1, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        uint32_t w0, w1;
+        prefetch(kt, w0, w1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(cur);
+        __builtin_amdgcn_sched_barrier(0);  // the MFMAs stay ahead of the wait
+        // all but the two prefetch loads just issued: this wave's part of the
+        // next stage has landed
+        __builtin_amdgcn_s_waitcnt(WAIT_VM2);
+        asm volatile("s_barrier" ::: "memory");
+        asm volatile("" ::"v"(pf_keep0), "v"(pf_keep1));
+        pf_keep0 = w0;
+        pf_keep1 = w1;
+    };
+    // one pipeline per state, always starting on stage0 (the stage of every
+    // access stays static, one copy of the loop); the boundary rescale stays
+    // out of the hot loop
     for (int s = kt0 / KTS; s < 3 && s * KTS < kt1; ++s) {
         const int ka = max(kt0, s * KTS), kb = min(kt1, (s + 1) * KTS);
-        for (int kt = ka; kt < kb; ++kt) body(kt);
+        issue(ka, stage0);
+        __builtin_amdgcn_s_waitcnt(0);
+        asm volatile("s_barrier" ::: "memory");
+        for (int kt = ka; kt < kb; kt += 2) {
+            step(kt, kb, stage0, stage1);
+            if (kt + 1 < kb) step(kt + 1, kb, stage1, stage0);
+        }
         if (!SPLIT && NORM != NORM_NONE && s < 2) rescale(s);
     }
+
+    asm volatile("" ::"v"(pf_keep0), "v"(pf_keep1));
 
     if (SPLIT) {
         // partial of this chunk in fragment order, then the last arriver sums
         const int splits = a.splits;
         const int tile = tc.mt * TN + tc.nt;
-        const size_t frag_per_wg = (size_t)PTH * 32;  // f32x4 per (tile, chunk)
+        const size_t frag_per_wg = (size_t)PTH * 64;  // f32x4 per (tile, chunk)
         f32x4* part = reinterpret_cast<f32x4*>(a.part);
         f32x4* mine = part + ((size_t)tile * splits + tc.chunk) * frag_per_wg;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             if (m0 + wm * 128 + 16 * i >= M) continue;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) mine[((size_t)(i * 4 + j) * 8 + wave) * 64 + lane] = acc[i][j];
+            for (int j = 0; j < 8; ++j) mine[((size_t)(i * 8 + j) * 4 + wave) * 64 + lane] = acc[i][j];
         }
         __threadfence();
         __syncthreads();
@@ -231,15 +298,15 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 8; ++j) {
                 f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
                 if (m0 + wm * 128 + 16 * i < M) {
                     for (int s = 0; s < 3; ++s) {
                         f32x4 ss = f32x4{0.f, 0.f, 0.f, 0.f};
                         for (int ch = s * kps; ch < (s + 1) * kps; ++ch)
-                            ss += part[((size_t)tile * splits + ch) * frag_per_wg + ((size_t)(i * 4 + j) * 8 + wave) * 64 +
+                            ss += part[((size_t)tile * splits + ch) * frag_per_wg + ((size_t)(i * 8 + j) * 4 + wave) * 64 +
                                        lane];
-                        const float uc = colf[s][wn * 64 + 16 * j + cb];
+                        const float uc = colf[s][wn * 128 + 16 * j + cb];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int rr = wm * 128 + 16 * i + 4 * g + e;
@@ -257,28 +324,28 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
         if (NORM != NORM_NONE) rescale(2);
     }
 
-    // + c, round to bf16, stage the wave's 128 x 64 tile in LDS, store 16-byte rows
-    float cc[4];
+    // + c, round to bf16, stage the wave's 128 x 128 tile in LDS, store 16-byte rows
+    float cc[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cc[j] = colf[3][wn * 64 + 16 * j + cb];
-    uint16_t* st = reinterpret_cast<uint16_t*>(lds) + (size_t)wave * 128 * 64;
+    for (int j = 0; j < 8; ++j) cc[j] = colf[3][wn * 128 + 16 * j + cb];
+    uint16_t* st = reinterpret_cast<uint16_t*>(wave < 2 ? stage0 : stage1) + (size_t)(wave & 1) * 128 * 128;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * i + 4 * g + e, col = 16 * j + cb;
-                st[r * 64 + col] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][j][e] + cc[j]));
+                st[r * 128 + col] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][j][e] + cc[j]));
             }
     __syncthreads();
 #pragma unroll 4
-    for (int v = lane; v < 128 * 8; v += 64) {
-        const int r = v >> 3, q = v & 7;
+    for (int v = lane; v < 128 * 16; v += 64) {
+        const int r = v >> 4, q = v & 15;
         const int m = m0 + wm * 128 + r;
-        const int n = n0 + wn * 64 + 8 * q;
+        const int n = n0 + wn * 128 + 8 * q;
         if (m < M && n < d)
-            *reinterpret_cast<uint4*>(a.out + (size_t)m * d + n) = *reinterpret_cast<const uint4*>(st + r * 64 + 8 * q);
+            *reinterpret_cast<uint4*>(a.out + (size_t)m * d + n) = *reinterpret_cast<const uint4*>(st + r * 128 + 8 * q);
     }
 }
 
@@ -297,7 +364,7 @@ PrefillPlan plan_prefill(int M, int d) {
     }
     if (p.splits > 1) {
         p.counters_bytes = ((size_t)tiles * sizeof(int) + 255) / 256 * 256;
-        p.part_bytes = (size_t)tiles * p.splits * PTH * 32 * sizeof(f32x4);
+        p.part_bytes = (size_t)tiles * p.splits * PTH * 64 * sizeof(f32x4);
     }
     return p;
 }
