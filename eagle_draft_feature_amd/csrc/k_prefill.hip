@@ -34,14 +34,18 @@ namespace e31 {
 
 constexpr int PBM = 256, PBN = 256, PBK = 64, PTH = 256;
 constexpr int PGM = 4;  // M-tiles per raster group
-constexpr int PFD = 3;  // L2 prefetch distance in k-tiles
-// s_waitcnt immediate: vmcnt <= 2, lgkmcnt = 0, expcnt not waited for
-constexpr int WAIT_VM2 = 2 | (7 << 4) | (0 << 8);
+constexpr int PFD = 4;  // L2 prefetch distance in k-tiles
+constexpr int PFW = 2;  // prefetch loads per thread and k-tile
+// s_waitcnt immediate: vmcnt <= n, lgkmcnt = 0, expcnt not waited for
+constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14); }
+constexpr int WAIT_VMPF = wait_vm(PFW);         // all but the prefetch just issued
+constexpr int WAIT_VMPF16 = wait_vm(PFW + 16);  // ... and one stage of LDS-DMA loads
+constexpr int WAIT_LGKM0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);  // lgkmcnt = 0 only
 constexpr int STAGE_A = PBM * PBK * 2;           // bytes of an A stage (32 KiB)
 constexpr int STAGE_BYTES = (PBM + PBN) * PBK * 2;  // A then B (64 KiB)
 
 struct TileCoord {
-    int mt, nt, chunk;
+    int mt, nt, chunk, gsz;  // gsz: M-tiles in the raster group of the tile
     bool valid;
 };
 
@@ -59,6 +63,7 @@ __device__ __forceinline__ TileCoord map_tile(int bid, int TM, int TN, int split
     const int within = tile - group * PGM * TN;
     tc.mt = first_m + within % gsz;
     tc.nt = within / gsz;
+    tc.gsz = gsz;
     return tc;
 }
 
@@ -124,25 +129,69 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
         }
     };
 
-    // L2 prefetch of k-tile kt + PFD: every CU of an XCD asks for the same new
+    // One of the wave's 16 LDS-DMA loads of a stage (c < 8: A block 8 w + c,
+    // else B tile 8 w + c - 8); hs: the A source of the k-tile (see issue).
+    auto issue_one = [&](int kt, const char* hs, char* sa, int c) __attribute__((always_inline)) {
+        if (c < 8) {
+            __builtin_amdgcn_global_load_lds(hs + aoff[c], sa + (8 * wave + c) * 1024, 16, 0, 0);
+        } else {
+            const int bt = 8 * wave + (c - 8);
+            const int nb = min((n0 >> 4) + (bt >> 1), nblk - 1);
+            const char* src = wbase + (((size_t)nb * T + 2 * kt + (bt & 1)) << 10);
+            __builtin_amdgcn_global_load_lds(src + boff, sa + STAGE_A + bt * 1024, 16, 0, 0);
+        }
+    };
+    auto a_src = [&](int kt) __attribute__((always_inline)) {
+        const int s = kt / KTS;
+        return reinterpret_cast<const char*>((s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2])) + (size_t)m0 * d +
+                                             (kt * PBK - s * d));
+    };
+
+    // L2 prefetch of k-tile kt + PFD.  Every CU of an XCD asks for the same new
     // k-slice at about the same time, so without it each k-tile pays the
-    // latency of memory, which one stage of lookahead cannot hide.  Thread t
-    // touches one dword of A row t and of B line t (16 lines of 128 bytes per
-    // column block): the whole k-slice of the tile.  The loaded words are
-    // kept until the next k-tile so that the wait at the end of a k-tile can
-    // leave the newest prefetch in flight.
-    const uint32_t pf_aoff = (uint32_t)(min(m0 + tid, M - 1) - m0) * (uint32_t)d * 2u;
-    const char* pf_b = wbase + ((size_t)min((n0 >> 4) + (tid >> 4), nblk - 1) * T << 10) + (tid & 15) * 128;
-    uint32_t pf_keep0 = 0, pf_keep1 = 0;
-    auto prefetch = [&](int kt, uint32_t& w0, uint32_t& w1) __attribute__((always_inline)) {
+    // latency of memory, which one stage of lookahead cannot hide.  A
+    // prefetch is one dword load per 128-byte line.  The workgroups an XCD
+    // runs together (a run of the raster order: up to 4 M-tiles x 8 N-tiles)
+    // share their A rows along N and their B lines along M, so each one
+    // touches only its share: A rows r with r = nt (mod amod), B lines with
+    // line = mt (mod bmod).  Split-K workgroups share nothing and touch their
+    // whole slice.  Lines are dealt round-robin over the waves, two per lane;
+    // lanes without one repeat the first line of their wave (one request).
+    // The loaded words are kept until a later wait has covered them.
+    int amod = 1, bmod = 1;
+    if (!SPLIT) {
+        const int na = min(TN, 8), nbm = tc.gsz;
+        amod = na >= 8 ? 8 : (na >= 4 ? 4 : (na >= 2 ? 2 : 1));
+        bmod = nbm >= 4 ? 4 : (nbm >= 2 ? 2 : 1);
+    }
+    bool pf_isa[PFW];
+    uint64_t pf_off[PFW];
+#pragma unroll
+    for (int h = 0; h < PFW; ++h) {
+        const int nA = PBM / amod, nT = nA + (16 * (PBN / 16)) / bmod;
+        int q = wave + 4 * lane + 256 * h;
+        if (q >= nT) q = wave;
+        if (q < nA) {
+            const int r = amod * q + tc.nt % amod;
+            pf_isa[h] = true;
+            pf_off[h] = (uint64_t)(min(m0 + r, M - 1) - m0) * (uint64_t)d * 2u;
+        } else {
+            const int L = bmod * (q - nA) + tc.mt % bmod;  // line of the B slice: 16 per column block
+            const int nb = min((n0 >> 4) + (L >> 4), nblk - 1);
+            pf_isa[h] = false;
+            pf_off[h] = ((uint64_t)nb * T << 10) + (uint64_t)(L & 15) * 128u;
+        }
+    }
+    auto prefetch = [&](int kt, uint32_t (&w)[PFW]) __attribute__((always_inline)) {
         const int kp = min(kt + PFD, kt1 - 1);
         const int s = kp / KTS;
-        const char* hs = reinterpret_cast<const char*>((s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2])) +
+        const char* ab = reinterpret_cast<const char*>((s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2])) +
                                                        (size_t)m0 * d + (kp * PBK - s * d));
-        w0 = __hip_atomic_load(reinterpret_cast<const uint32_t*>(hs + pf_aoff), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
-        w1 = __hip_atomic_load(reinterpret_cast<const uint32_t*>(pf_b + ((size_t)kp << 11)), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
+        const char* bb = wbase + ((size_t)kp << 11);
+#pragma unroll
+        for (int h = 0; h < PFW; ++h)
+            w[h] = __hip_atomic_load(reinterpret_cast<const uint32_t*>((pf_isa[h] ? ab : bb) + pf_off[h]),
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
 
     // fragment reads: A row wm 128 + 16 i + lane % 16, chunk 4 kk + lane / 16;
@@ -210,48 +259,89 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
         }
     };
 
-    // all 32 fragment reads of the k-tile first (128 VGPRs), then the 128 MFMAs,
-    // so the LDS latency is paid once per k-tile rather than per row block
-    // all 32 fragment reads of the k-tile first (128 VGPRs), then the 128 MFMAs,
-    // so the LDS latency is paid once per k-tile rather than per row block
-    auto compute = [&](const char* sa) __attribute__((always_inline)) {
-        u32x4 bfr[2][8], af[2][8];
+    // Fragments of one k-step (kk) of a stage: 8 B and 8 A operands (64 VGPRs).
+    auto read_frags = [&](const char* sa, int kk, u32x4 (&fa)[8], u32x4 (&fb)[8]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int j = 0; j < 8; ++j) fb[j] = *reinterpret_cast<const u32x4*>(sa + bread + (2 * j + kk) * 1024);
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                bfr[kk][j] = *reinterpret_cast<const u32x4*>(sa + bread + (2 * j + kk) * 1024);
+        for (int i = 0; i < 8; ++i) fa[i] = *reinterpret_cast<const u32x4*>(sa + aread[kk] + 2048 * i);
+    };
+    auto mma = [&](const u32x4 (&fa)[8], const u32x4 (&fb)[8]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) af[kk][i] = *reinterpret_cast<const u32x4*>(sa + aread[kk] + 2048 * i);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = mfma16x16x32(af[kk][i], bfr[kk][j], acc[i][j]);
+            for (int j = 0; j < 8; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
     };
 
-    // k-tile kt of a state ending at kb: load kt + 1 into the other stage, MFMAs
-    // on this one, then wait for that load and for every wave to be done with
-    // this stage.  The barrier is a bare s_barrier: a fence would also wait for
-    // the L2 prefetch still in flight.
+    // Software pipeline of one state (k-tiles ka .. kb-1), two stages X, Y:
+    // step kt (stage cur holds kt, nxt holds kt + 1, F0 = its kk = 0 operands):
+    //   64 MFMAs on F0, with the 16 reads of F1 (kk = 1 of cur) between them
+    //   wait for this wave's loads of nxt and for its LDS reads; barrier
+    //   (every wave is done with cur, nxt has landed)
+    //   64 MFMAs on F1, with the 16 LDS-DMA loads of kt + 2 into cur and the 16
+    //   reads of F0 of nxt between them; then the L2 prefetch
+    // One memory instruction per 4 MFMAs keeps the address and LDS queues
+    // short, so the waves never stall at issue with the MFMA pipe idle.  The
+    // barrier is a bare s_barrier (the explicit wait above covers the loads it
+    // needs): a fence would also wait for the L2 prefetch still in flight.  The
+    // prefetch loads are always the last memory instructions before a wait,
+    // which leaves them in flight; their words are kept two steps, until a
+    // wait that has covered them.  Near the end of a state the loads re-read
+    // the last k-tile and the reads fetch a stale stage: harmless, and the
+    // loop body stays free of branches.
+    u32x4 fa0[8], fb0[8], fa1[8], fb1[8];
+    uint32_t keep[2][PFW];
+#pragma unroll
+    for (int q = 0; q < PFW; ++q) keep[0][q] = keep[1][q] = 0u;
+    auto prefetch_keep = [&](int kt) __attribute__((always_inline)) {
+        uint32_t w[PFW];
+        prefetch(kt, w);
+#pragma unroll
+        for (int q = 0; q < PFW; ++q) {
+            keep[0][q] = keep[1][q];
+            keep[1][q] = w[q];
+        }
+    };
+    auto consume = [&](const uint32_t (&k)[PFW]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < PFW; ++q) asm volatile("" ::"v"(k[q]));
+    };
+    // read c of a k-step's fragments (c < 8: B operand c, else A operand c - 8)
+    auto read_one = [&](const char* sa, int kk, u32x4 (&fa)[8], u32x4 (&fb)[8], int c) __attribute__((always_inline)) {
+        if (c < 8)
+            fb[c] = *reinterpret_cast<const u32x4*>(sa + bread + (2 * c + kk) * 1024);
+        else
+            fa[c - 8] = *reinterpret_cast<const u32x4*>(sa + aread[kk] + 2048 * (c - 8));
+    };
+    // MFMAs 4 c .. 4 c + 3 of a k-step: row block c / 2, column blocks 4 (c % 2) ..
+    auto mma4 = [&](const u32x4 (&fa)[8], const u32x4 (&fb)[8], int c) __attribute__((always_inline)) {
+        const int i = c >> 1;
+#pragma unroll
+        for (int j = 4 * (c & 1); j < 4 * (c & 1) + 4; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+    };
     auto step = [&](int kt, int kb, char* cur, char* nxt) __attribute__((always_inline)) {
-        if (kt + 1 < kb) issue(kt + 1, nxt);
-        __builtin_amdgcn_sched_barrier(0);
-        uint32_t w0, w1;
-        prefetch(kt, w0, w1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(cur);
-        __builtin_amdgcn_sched_barrier(0);  // the MFMAs stay ahead of the wait
-        // all but the two prefetch loads just issued: this wave's part of the
-        // next stage has landed
-        __builtin_amdgcn_s_waitcnt(WAIT_VM2);
+        // F0 has landed (it was read during the previous MFMA half)
+        __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            read_one(cur, 1, fa1, fb1, c);
+            mma4(fa0, fb0, c);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt(WAIT_VMPF);
         asm volatile("s_barrier" ::: "memory");
-        asm volatile("" ::"v"(pf_keep0), "v"(pf_keep1));
-        pf_keep0 = w0;
-        pf_keep1 = w1;
+        consume(keep[0]);  // the prefetch of two steps ago has landed
+        const int kn = min(kt + 2, kb - 1);
+        const char* hs = a_src(kn);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            issue_one(kn, hs, cur, c);
+            read_one(nxt, 0, fa0, fb0, c);
+            mma4(fa1, fb1, c);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        prefetch_keep(kt);
+        __builtin_amdgcn_sched_barrier(0);
     };
     // one pipeline per state, always starting on stage0 (the stage of every
     // access stays static, one copy of the loop); the boundary rescale stays
@@ -259,16 +349,29 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
     for (int s = kt0 / KTS; s < 3 && s * KTS < kt1; ++s) {
         const int ka = max(kt0, s * KTS), kb = min(kt1, (s + 1) * KTS);
         issue(ka, stage0);
-        __builtin_amdgcn_s_waitcnt(0);
+        if (ka + 1 < kb) issue(ka + 1, stage1);
+        __builtin_amdgcn_sched_barrier(0);
+        prefetch_keep(ka - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // stage0 has landed (the loads of stage1 and the prefetch may not have)
+        if (ka + 1 < kb)
+            __builtin_amdgcn_s_waitcnt(WAIT_VMPF16);
+        else
+            __builtin_amdgcn_s_waitcnt(WAIT_VMPF);
         asm volatile("s_barrier" ::: "memory");
+        read_frags(stage0, 0, fa0, fb0);
         for (int kt = ka; kt < kb; kt += 2) {
             step(kt, kb, stage0, stage1);
             if (kt + 1 < kb) step(kt + 1, kb, stage1, stage0);
         }
         if (!SPLIT && NORM != NORM_NONE && s < 2) rescale(s);
     }
-
-    asm volatile("" ::"v"(pf_keep0), "v"(pf_keep1));
+    consume(keep[0]);
+    consume(keep[1]);
+    // the last steps' loads write the stages the epilogue reuses: all of them
+    // land before any wave writes there
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 
     if (SPLIT) {
         // partial of this chunk in fragment order, then the last arriver sums
