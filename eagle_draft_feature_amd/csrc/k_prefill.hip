@@ -32,17 +32,37 @@
 
 namespace e31 {
 
-constexpr int PBM = 256, PBN = 256, PBK = 64, PTH = 256;
-constexpr int PGM = 4;  // M-tiles per raster group
-constexpr int PFD = 4;  // L2 prefetch distance in k-tiles
-constexpr int PFW = 2;  // prefetch loads per thread and k-tile
-// s_waitcnt immediate: vmcnt <= n, lgkmcnt = 0, expcnt not waited for
+constexpr int PBM = 256, PBN = 256, PBK = 32, PTH = 256;  // PBK: k per sub-tile (one MFMA k-step)
+constexpr int NST = 4;   // LDS stages
+constexpr int PGM = 4;   // M-tiles per raster group
+constexpr int STAGE_A = PBM * PBK * 2;              // A part of a stage (16 KiB)
+constexpr int STAGE_BYTES = (PBM + PBN) * PBK * 2;  // A then B (32 KiB)
+// s_waitcnt immediates: vmcnt <= n with lgkmcnt = 0; lgkmcnt = 0 alone
 constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (0 << 8) | ((n >> 4) << 14); }
-constexpr int WAIT_VMPF = wait_vm(PFW);         // all but the prefetch just issued
-constexpr int WAIT_VMPF16 = wait_vm(PFW + 16);  // ... and one stage of LDS-DMA loads
-constexpr int WAIT_LGKM0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);  // lgkmcnt = 0 only
-constexpr int STAGE_A = PBM * PBK * 2;           // bytes of an A stage (32 KiB)
-constexpr int STAGE_BYTES = (PBM + PBN) * PBK * 2;  // A then B (64 KiB)
+constexpr int WAIT_LGKM0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+// LDS-DMA loads written as inline asm, so that the compiler sees no vector
+// memory operation in the main loop: it then inserts no waits of its own
+// (its alias analysis cannot always separate the stage a load writes from the
+// stage being read), and the explicit waits, derived from the fixed issue
+// order, are the only ones.  The asm writes M0, which nothing else in the
+// kernel uses.  16 bytes per lane from sbase + voff (sbase wave-uniform) to
+// LDS byte lds + 16 lane:
+// (readfirstlane pins the wave-uniform operands to scalar registers; the
+// compiler drops it where they already are)
+__device__ __forceinline__ uint64_t uniform64(const void* p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(__builtin_amdgcn_readfirstlane(lds)),
+                 "v"(voff), "s"(uniform64(sbase))
+                 : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
 struct TileCoord {
     int mt, nt, chunk, gsz;  // gsz: M-tiles in the raster group of the tile
@@ -69,24 +89,28 @@ __device__ __forceinline__ TileCoord map_tile(int bid, int TM, int TN, int split
 
 template <bool SPLIT, int NORM>
 __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, int TN) {
-    // two stages in separate arrays: with static stage indices the compiler
-    // can tell the LDS-DMA writes of one stage from the reads of the other
-    __shared__ __attribute__((aligned(1024))) char stage0[STAGE_BYTES];
-    __shared__ __attribute__((aligned(1024))) char stage1[STAGE_BYTES];
+    // four stages in separate arrays: with static stage indices the compiler
+    // can tell the LDS-DMA writes of one stage from the reads of another
+    __shared__ __attribute__((aligned(1024))) char st0[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st1[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st2[STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) char st3[STAGE_BYTES];
     // per-row factors of the tile: mu_0, rstd_0/rstd_1, mu_1, rstd_1/rstd_2, mu_2, rstd_2
     // per-column factors: u_0, u_1, u_2, c
     __shared__ float rowf[6][PBM];
     __shared__ float colf[4][PBN];
+    // end of a sub-step: the stage of sub-tile u + 2 has landed, i.e. all but
+    // the newest 2 stages of loads (8 per wave each) are complete
+    constexpr int WAIT_STAGE = wait_vm(16);
 
     const TileCoord tc = map_tile(blockIdx.x, TM, TN, SPLIT ? a.splits : 1);
     if (!tc.valid) return;
     const int M = a.M, d = a.d;
-    const size_t K3 = (size_t)3 * d;
     const int m0 = tc.mt * PBM, n0 = tc.nt * PBN;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, cb = lane & 15;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave bases stay scalar
     const int wm = wave >> 1, wn = wave & 1;
-    const int KTS = d / PBK;  // k-tiles per state
+    const int KTS = d / PBK;  // sub-tiles per state
     int kt0 = 0, kt1 = 3 * KTS;
     if (SPLIT) {
         const int kps = a.splits / 3;
@@ -95,115 +119,44 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
         kt1 = s * KTS + ((j + 1) * KTS) / kps;
     }
 
-    // Loader roles (per stage, 32 A blocks and 32 B tiles of 1 KiB; wave w
-    // issues A blocks and B tiles 8 w .. 8 w + 7):
-    //  A block ab: rows 8 ab + lane / 8, LDS chunk lane % 8 holds global
-    //  chunk (lane % 8) ^ ((row / 2) % 8); rows past M re-read row M - 1.
-    //  B tile bt: column block n0 / 16 + bt / 2 (clamped), k-step 2 kt + bt % 2.
+    // Loads of a stage (16 A blocks and 16 B tiles of 1 KiB; wave w issues
+    // A blocks and B tiles 4 w .. 4 w + 3), one LDS-DMA instruction each:
+    //  A block ab: rows 16 ab + lane / 4, LDS chunk lane % 4 holds global
+    //  chunk (lane % 4) ^ ((row / 4) % 4); rows past M re-read row M - 1.
+    //  B tile bt: column block n0 / 16 + bt (clamped), k-step u.
     // Addresses are a wave-uniform base plus a 32-bit per-lane byte offset.
-    const int T = (int)(K3 / 32);  // tiles per column block
+    const int T = 3 * KTS;  // tiles per column block
     const int nblk = d >> 4;
-    uint32_t aoff[8];
+    uint32_t aoff[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int r = 8 * (8 * wave + q) + (lane >> 3);
-        const int c = (lane & 7) ^ ((r >> 1) & 7);
+    for (int q = 0; q < 4; ++q) {
+        const int r = 16 * (4 * wave + q) + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 2) & 3);
         aoff[q] = (uint32_t)((min(m0 + r, M - 1) - m0) * d + 8 * c) * 2u;  // < 512 d bytes
     }
     const char* wbase = reinterpret_cast<const char*>(a.wt);
     const uint32_t boff = (uint32_t)lane * 16u;
-    auto issue = [&](int kt, char* sa) __attribute__((always_inline)) {
-        const int s = kt / KTS;
-        const char* hs = reinterpret_cast<const char*>((s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2])) +
-                                                       (size_t)m0 * d + (kt * PBK - s * d));
-        char* sb = sa + STAGE_A;
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-            __builtin_amdgcn_global_load_lds(hs + aoff[q], sa + (8 * wave + q) * 1024, 16, 0, 0);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int bt = 8 * wave + q;
-            const int nb = min((n0 >> 4) + (bt >> 1), nblk - 1);
-            const char* src = wbase + (((size_t)nb * T + 2 * kt + (bt & 1)) << 10);
-            __builtin_amdgcn_global_load_lds(src + boff, sb + bt * 1024, 16, 0, 0);
-        }
-    };
-
-    // One of the wave's 16 LDS-DMA loads of a stage (c < 8: A block 8 w + c,
-    // else B tile 8 w + c - 8); hs: the A source of the k-tile (see issue).
-    auto issue_one = [&](int kt, const char* hs, char* sa, int c) __attribute__((always_inline)) {
-        if (c < 8) {
-            __builtin_amdgcn_global_load_lds(hs + aoff[c], sa + (8 * wave + c) * 1024, 16, 0, 0);
-        } else {
-            const int bt = 8 * wave + (c - 8);
-            const int nb = min((n0 >> 4) + (bt >> 1), nblk - 1);
-            const char* src = wbase + (((size_t)nb * T + 2 * kt + (bt & 1)) << 10);
-            __builtin_amdgcn_global_load_lds(src + boff, sa + STAGE_A + bt * 1024, 16, 0, 0);
-        }
-    };
-    auto a_src = [&](int kt) __attribute__((always_inline)) {
-        const int s = kt / KTS;
+    auto a_src = [&](int u) __attribute__((always_inline)) {
+        const int s = u >= 2 * KTS ? 2 : (u >= KTS ? 1 : 0);
         return reinterpret_cast<const char*>((s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2])) + (size_t)m0 * d +
-                                             (kt * PBK - s * d));
+                                             (u * PBK - s * d));
     };
-
-    // L2 prefetch of k-tile kt + PFD.  Every CU of an XCD asks for the same new
-    // k-slice at about the same time, so without it each k-tile pays the
-    // latency of memory, which one stage of lookahead cannot hide.  A
-    // prefetch is one dword load per 128-byte line.  The workgroups an XCD
-    // runs together (a run of the raster order: up to 4 M-tiles x 8 N-tiles)
-    // share their A rows along N and their B lines along M, so each one
-    // touches only its share: A rows r with r = nt (mod amod), B lines with
-    // line = mt (mod bmod).  Split-K workgroups share nothing and touch their
-    // whole slice.  Lines are dealt round-robin over the waves, two per lane;
-    // lanes without one repeat the first line of their wave (one request).
-    // The loaded words are kept until a later wait has covered them.
-    int amod = 1, bmod = 1;
-    if (!SPLIT) {
-        const int na = min(TN, 8), nbm = tc.gsz;
-        amod = na >= 8 ? 8 : (na >= 4 ? 4 : (na >= 2 ? 2 : 1));
-        bmod = nbm >= 4 ? 4 : (nbm >= 2 ? 2 : 1);
-    }
-    bool pf_isa[PFW];
-    uint64_t pf_off[PFW];
-#pragma unroll
-    for (int h = 0; h < PFW; ++h) {
-        const int nA = PBM / amod, nT = nA + (16 * (PBN / 16)) / bmod;
-        int q = wave + 4 * lane + 256 * h;
-        if (q >= nT) q = wave;
-        if (q < nA) {
-            const int r = amod * q + tc.nt % amod;
-            pf_isa[h] = true;
-            pf_off[h] = (uint64_t)(min(m0 + r, M - 1) - m0) * (uint64_t)d * 2u;
+    // load c (< 8) of the wave's share of sub-tile u into stage sa; hs = a_src(u)
+    auto issue_one = [&](int u, const char* hs, char* sa, int c) __attribute__((always_inline)) {
+        if (c < 4) {
+            dma16(hs, aoff[c], lds_addr(sa + (4 * wave + c) * 1024));
         } else {
-            const int L = bmod * (q - nA) + tc.mt % bmod;  // line of the B slice: 16 per column block
-            const int nb = min((n0 >> 4) + (L >> 4), nblk - 1);
-            pf_isa[h] = false;
-            pf_off[h] = ((uint64_t)nb * T << 10) + (uint64_t)(L & 15) * 128u;
+            const int bt = 4 * wave + (c - 4);
+            const int nb = min((n0 >> 4) + bt, nblk - 1);
+            dma16(wbase + (((size_t)nb * T + u) << 10), boff, lds_addr(sa + STAGE_A + bt * 1024));
         }
-    }
-    auto prefetch = [&](int kt, uint32_t (&w)[PFW]) __attribute__((always_inline)) {
-        const int kp = min(kt + PFD, kt1 - 1);
-        const int s = kp / KTS;
-        const char* ab = reinterpret_cast<const char*>((s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2])) +
-                                                       (size_t)m0 * d + (kp * PBK - s * d));
-        const char* bb = wbase + ((size_t)kp << 11);
-#pragma unroll
-        for (int h = 0; h < PFW; ++h)
-            w[h] = __hip_atomic_load(reinterpret_cast<const uint32_t*>((pf_isa[h] ? ab : bb) + pf_off[h]),
-                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     };
 
-    // fragment reads: A row wm 128 + 16 i + lane % 16, chunk 4 kk + lane / 16;
-    // the swizzle (row / 2) % 8 is the same for the 8 row blocks, so one base
-    // per kk and an immediate offset of 2048 i bytes
-    uint32_t aread[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        const int r = wm * 128 + cb;
-        aread[kk] = (uint32_t)(r * 128 + 16 * ((4 * kk + g) ^ ((r >> 1) & 7)));
-    }
-    const uint32_t bread = (uint32_t)(STAGE_A + wn * 16384) + (uint32_t)lane * 16u;
+    // fragment reads: A row wm 128 + 16 i + lane % 16, chunk lane / 16; the
+    // swizzle (row / 4) % 4 is the same for the 8 row blocks, so one base and
+    // an immediate offset of 1024 i bytes.  B tile wn 8 + j, lane's 16 bytes.
+    const uint32_t aread = (uint32_t)((wm * 128 + cb) * 64 + 16 * (g ^ ((cb >> 2) & 3)));
+    const uint32_t bread = (uint32_t)(STAGE_A + wn * 8192) + (uint32_t)lane * 16u;
 
     f32x4 acc[8][8];
 #pragma unroll
@@ -259,119 +212,85 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
         }
     };
 
-    // Fragments of one k-step (kk) of a stage: 8 B and 8 A operands (64 VGPRs).
-    auto read_frags = [&](const char* sa, int kk, u32x4 (&fa)[8], u32x4 (&fb)[8]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) fb[j] = *reinterpret_cast<const u32x4*>(sa + bread + (2 * j + kk) * 1024);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) fa[i] = *reinterpret_cast<const u32x4*>(sa + aread[kk] + 2048 * i);
-    };
-    auto mma = [&](const u32x4 (&fa)[8], const u32x4 (&fb)[8]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
-    };
-
-    // Software pipeline of one state (k-tiles ka .. kb-1), two stages X, Y:
-    // step kt (stage cur holds kt, nxt holds kt + 1, F0 = its kk = 0 operands):
-    //   64 MFMAs on F0, with the 16 reads of F1 (kk = 1 of cur) between them
-    //   wait for this wave's loads of nxt and for its LDS reads; barrier
-    //   (every wave is done with cur, nxt has landed)
-    //   64 MFMAs on F1, with the 16 LDS-DMA loads of kt + 2 into cur and the 16
-    //   reads of F0 of nxt between them; then the L2 prefetch
-    // One memory instruction per 4 MFMAs keeps the address and LDS queues
-    // short, so the waves never stall at issue with the MFMA pipe idle.  The
-    // barrier is a bare s_barrier (the explicit wait above covers the loads it
-    // needs): a fence would also wait for the L2 prefetch still in flight.  The
-    // prefetch loads are always the last memory instructions before a wait,
-    // which leaves them in flight; their words are kept two steps, until a
-    // wait that has covered them.  Near the end of a state the loads re-read
-    // the last k-tile and the reads fetch a stale stage: harmless, and the
-    // loop body stays free of branches.
-    u32x4 fa0[8], fb0[8], fa1[8], fb1[8];
-    uint32_t keep[2][PFW];
-#pragma unroll
-    for (int q = 0; q < PFW; ++q) keep[0][q] = keep[1][q] = 0u;
-    auto prefetch_keep = [&](int kt) __attribute__((always_inline)) {
-        uint32_t w[PFW];
-        prefetch(kt, w);
-#pragma unroll
-        for (int q = 0; q < PFW; ++q) {
-            keep[0][q] = keep[1][q];
-            keep[1][q] = w[q];
-        }
-    };
-    auto consume = [&](const uint32_t (&k)[PFW]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int q = 0; q < PFW; ++q) asm volatile("" ::"v"(k[q]));
-    };
-    // read c of a k-step's fragments (c < 8: B operand c, else A operand c - 8)
-    auto read_one = [&](const char* sa, int kk, u32x4 (&fa)[8], u32x4 (&fb)[8], int c) __attribute__((always_inline)) {
+    // Pipeline of one state (sub-tiles ua .. ub-1) over four stages; stage v
+    // (mod 4) of the state holds sub-tile ua + v.  Sub-step u, with F(u) (its
+    // 8 A and 8 B operands) already in registers:
+    //   64 MFMAs on F(u); between them, the 16 reads of F(u + 1), one per 4
+    //   MFMAs, and the 8 loads of sub-tile u + 4 into the stage of u (free:
+    //   every wave read F(u) before the last barrier), one per 8; then
+    //   wait for the stage of u + 2 and the reads; barrier.
+    // A stage is needed 2 to 3 sub-steps after its loads are issued.  The
+    // barrier is a bare s_barrier (the explicit wait covers what it needs).
+    // Each sub-step issues exactly 8 loads per wave, so one vmcnt bound fits
+    // every wait; near the end of a state the loads re-read the last sub-tile
+    // and the reads may fetch a stale stage: harmless, and the body has no
+    // branches.
+    u32x4 fA[2][8], fB[2][8];  // two register sets of operands
+    // read c of sub-tile operands (c < 8: B operand c, else A operand c - 8)
+    auto read_one = [&](const char* sa, int set, int c) __attribute__((always_inline)) {
         if (c < 8)
-            fb[c] = *reinterpret_cast<const u32x4*>(sa + bread + (2 * c + kk) * 1024);
+            fB[set][c] = *reinterpret_cast<const u32x4*>(sa + bread + c * 1024);
         else
-            fa[c - 8] = *reinterpret_cast<const u32x4*>(sa + aread[kk] + 2048 * (c - 8));
+            fA[set][c - 8] = *reinterpret_cast<const u32x4*>(sa + aread + 1024 * (c - 8));
     };
-    // MFMAs 4 c .. 4 c + 3 of a k-step: row block c / 2, column blocks 4 (c % 2) ..
-    auto mma4 = [&](const u32x4 (&fa)[8], const u32x4 (&fb)[8], int c) __attribute__((always_inline)) {
-        const int i = c >> 1;
-#pragma unroll
-        for (int j = 4 * (c & 1); j < 4 * (c & 1) + 4; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
-    };
-    auto step = [&](int kt, int kb, char* cur, char* nxt) __attribute__((always_inline)) {
-        // F0 has landed (it was read during the previous MFMA half)
+    auto sub_step = [&](int u, int lim, char* cur, char* nxt, int set) __attribute__((always_inline)) {
+        // F(u) has landed (read during the previous sub-step)
         __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+        const int un = min(u + 4, lim - 1);
+        const char* hs = a_src(un);
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
-            read_one(cur, 1, fa1, fb1, c);
-            mma4(fa0, fb0, c);
+            if ((c & 1) == 0) issue_one(un, hs, cur, c >> 1);
+            read_one(nxt, set ^ 1, c);
+            const int i = c >> 1;
+#pragma unroll
+            for (int j = 4 * (c & 1); j < 4 * (c & 1) + 4; ++j)
+                acc[i][j] = mfma16x16x32(fA[set][i], fB[set][j], acc[i][j]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_s_waitcnt(WAIT_VMPF);
+        __builtin_amdgcn_s_waitcnt(WAIT_STAGE);
         asm volatile("s_barrier" ::: "memory");
-        consume(keep[0]);  // the prefetch of two steps ago has landed
-        const int kn = min(kt + 2, kb - 1);
-        const char* hs = a_src(kn);
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            issue_one(kn, hs, cur, c);
-            read_one(nxt, 0, fa0, fb0, c);
-            mma4(fa1, fb1, c);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        prefetch_keep(kt);
-        __builtin_amdgcn_sched_barrier(0);
     };
-    // one pipeline per state, always starting on stage0 (the stage of every
-    // access stays static, one copy of the loop); the boundary rescale stays
-    // out of the hot loop
+    // When every state's sub-tile count is a multiple of 4 (and always for a
+    // split-K chunk, which lies in one state), the pipeline runs on across the
+    // state boundaries: the loads near the end of a state already fetch the
+    // next one and each state starts on stage 0 again.  Otherwise it restarts
+    // at every state.
+    const bool cont = SPLIT || (KTS & 3) == 0;
     for (int s = kt0 / KTS; s < 3 && s * KTS < kt1; ++s) {
-        const int ka = max(kt0, s * KTS), kb = min(kt1, (s + 1) * KTS);
-        issue(ka, stage0);
-        if (ka + 1 < kb) issue(ka + 1, stage1);
-        __builtin_amdgcn_sched_barrier(0);
-        prefetch_keep(ka - 1);
-        __builtin_amdgcn_sched_barrier(0);
-        // stage0 has landed (the loads of stage1 and the prefetch may not have)
-        if (ka + 1 < kb)
-            __builtin_amdgcn_s_waitcnt(WAIT_VMPF16);
-        else
-            __builtin_amdgcn_s_waitcnt(WAIT_VMPF);
-        asm volatile("s_barrier" ::: "memory");
-        read_frags(stage0, 0, fa0, fb0);
-        for (int kt = ka; kt < kb; kt += 2) {
-            step(kt, kb, stage0, stage1);
-            if (kt + 1 < kb) step(kt + 1, kb, stage1, stage0);
+        const int ua = max(kt0, s * KTS), ub = min(kt1, (s + 1) * KTS);
+        const int lim = cont ? kt1 : ub;  // loads stay below lim
+        if (!cont || ua == kt0) {
+            // prologue: sub-tiles ua .. ua+3 (clamped) into stages 0..3
+            char* const stv[4] = {st0, st1, st2, st3};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int uv = min(ua + v, lim - 1);
+                const char* hs = a_src(uv);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) issue_one(uv, hs, stv[v], c);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // stages 0 and 1 have landed; F(ua) from stage 0
+            __builtin_amdgcn_s_waitcnt(WAIT_STAGE);
+            asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+            for (int c = 0; c < 16; ++c) read_one(st0, 0, c);
+            // every wave has its F(ua) before sub-step ua reloads stage 0
+            __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+            asm volatile("s_barrier" ::: "memory");
+        }
+        for (int u = ua; u < ub; u += 4) {
+            sub_step(u, lim, st0, st1, 0);
+            if (u + 1 < ub) sub_step(u + 1, lim, st1, st2, 1);
+            if (u + 2 < ub) sub_step(u + 2, lim, st2, st3, 0);
+            if (u + 3 < ub) sub_step(u + 3, lim, st3, st0, 1);
         }
         if (!SPLIT && NORM != NORM_NONE && s < 2) rescale(s);
     }
-    consume(keep[0]);
-    consume(keep[1]);
-    // the last steps' loads write the stages the epilogue reuses: all of them
-    // land before any wave writes there
+    // the last sub-steps' loads (re-reads near the end) land before the
+    // workgroup can end and its LDS be handed to another
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
 
     if (SPLIT) {
         // partial of this chunk in fragment order, then the last arriver sums
@@ -427,28 +346,38 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
         if (NORM != NORM_NONE) rescale(2);
     }
 
-    // + c, round to bf16, stage the wave's 128 x 128 tile in LDS, store 16-byte rows
-    float cc[8];
+    // + c, round to bf16 and store.  Lane (g, cb) holds rows 4 g + e (e < 4)
+    // of column cb of each 16 x 16 block.  Two exchanges inside each quad of
+    // lanes (cb = 4 k + t; partners t ^ 1, then t ^ 2) leave lane t with one
+    // row, ((t & 1) << 1) | (t >> 1), and the quad's 4 columns 4 k .. 4 k + 3:
+    // one 8-byte store, no staging through LDS.
+    {
+        const int t = cb & 3, k4 = cb >> 2;
+        const bool odd = (t & 1) != 0, hi = t >= 2;
+        const int rl = ((t & 1) << 1) | (t >> 1);
+        auto swap1 = [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)); };
+        auto swap2 = [](uint32_t x) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false); };
+        float cc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) cc[j] = colf[3][wn * 128 + 16 * j + cb];
-    uint16_t* st = reinterpret_cast<uint16_t*>(wave < 2 ? stage0 : stage1) + (size_t)(wave & 1) * 128 * 128;
+        for (int j = 0; j < 8; ++j) cc[j] = colf[3][wn * 128 + 16 * j + cb];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 8; ++i) {
+            const int m = m0 + wm * 128 + 16 * i + 4 * g + rl;
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * i + 4 * g + e, col = 16 * j + cb;
-                st[r * 128 + col] = __builtin_bit_cast(uint16_t, (__bf16)(acc[i][j][e] + cc[j]));
+            for (int j = 0; j < 8; ++j) {
+                const float v0 = acc[i][j][0] + cc[j], v1 = acc[i][j][1] + cc[j];
+                const float v2 = acc[i][j][2] + cc[j], v3 = acc[i][j][3] + cc[j];
+                // even lanes keep rows 0, 1 and odd lanes rows 2, 3 of the pair's two columns
+                const float r0 = swap1(odd ? v0 : v2), r1 = swap1(odd ? v1 : v3);
+                const uint32_t P0 = odd ? pack_bf2(r0, v2) : pack_bf2(v0, r0);
+                const uint32_t P1 = odd ? pack_bf2(r1, v3) : pack_bf2(v1, r1);
+                // then each lane keeps one row of the quad's four columns
+                const uint32_t rv = swap2(hi ? P0 : P1);
+                const uint2 w = hi ? make_uint2(rv, P1) : make_uint2(P0, rv);
+                const int n = n0 + wn * 128 + 16 * j + 4 * k4;
+                if (m < M && n < d) *reinterpret_cast<uint2*>(a.out + (size_t)m * d + n) = w;
             }
-    __syncthreads();
-#pragma unroll 4
-    for (int v = lane; v < 128 * 16; v += 64) {
-        const int r = v >> 4, q = v & 15;
-        const int m = m0 + wm * 128 + r;
-        const int n = n0 + wn * 128 + 8 * q;
-        if (m < M && n < d)
-            *reinterpret_cast<uint4*>(a.out + (size_t)m * d + n) = *reinterpret_cast<const uint4*>(st + r * 128 + 8 * q);
+        }
     }
 }
 
