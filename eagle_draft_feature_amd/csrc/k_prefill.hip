@@ -5,11 +5,12 @@
 // llm-wiki.hwlabs.dev/study/dist/ai-frontier/76.html, section
 // "FC 정규화: EAGLE 3.1의 핵심 수정": the parameters are absorbed by the FC),
 //     out = sum_s rstd_s * (h_s . W'_s^T - mu_s * u_s) + c,
-// so the main loop is a plain GEMM over the three states in turn, and the normalisation is a per-row rescale of the
-// accumulator at each state boundary:
-//     acc <- (acc - mu_s * u_s) * rstd_s / rstd_{s+1},
-// finished by acc <- (acc - mu_2 * u_2) * rstd_2 + c.  The statistics come
-// from the row-statistics pass that runs first.
+// so the main loop is a plain GEMM over the three states in turn.  The
+// accumulator is scaled per row by rstd_s / rstd_{s+1} at each state
+// boundary, so it ends as sum_s rstd_s h_s . W'_s; the epilogue multiplies by
+// rstd_2 and subtracts the rank-3 mean term sum_s (rstd_s mu_s) u_s before
+// adding c.  The statistics come from the row-statistics pass that runs
+// first.
 //
 // Tiling for gfx950: 256 x 256 output tile, BK = 64, 256 threads (4 waves
 // as 2 x 2, each wave 128 x 128 = 8 x 8 MFMA 16x16x32 blocks, whose 256
@@ -166,17 +167,29 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
 
     if (tid < PBM) {
         const int m = m0 + tid;
-        float f[6] = {0.f, 1.f, 0.f, 1.f, 0.f, 1.f};
+        float r[3] = {1.f, 1.f, 1.f}, mu[3] = {0.f, 0.f, 0.f};
         if (m < M && NORM != NORM_NONE) {
-            const float r0 = a.rstd[m], r1 = a.rstd[(size_t)M + m], r2 = a.rstd[(size_t)2 * M + m];
-            if (NORM == NORM_LN) {
-                f[0] = a.mu[m];
-                f[2] = a.mu[(size_t)M + m];
-                f[4] = a.mu[(size_t)2 * M + m];
+#pragma unroll
+            for (int q = 0; q < 3; ++q) r[q] = a.rstd[(size_t)q * M + m];
+            if (NORM == NORM_LN)
+#pragma unroll
+                for (int q = 0; q < 3; ++q) mu[q] = a.mu[(size_t)q * M + m];
+        }
+        float f[6];
+        if (SPLIT) {
+            // mu_0, rstd_0, mu_1, rstd_1, mu_2, rstd_2
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                f[2 * q] = mu[q];
+                f[2 * q + 1] = r[q];
             }
-            f[1] = SPLIT ? r0 : r0 / r1;
-            f[3] = SPLIT ? r1 : r1 / r2;
-            f[5] = r2;
+        } else {
+            // rstd_0/rstd_1, rstd_1/rstd_2, rstd_2, rstd_0 mu_0, rstd_1 mu_1, rstd_2 mu_2
+            f[0] = r[0] / r[1];
+            f[1] = r[1] / r[2];
+            f[2] = r[2];
+#pragma unroll
+            for (int q = 0; q < 3; ++q) f[3 + q] = r[q] * mu[q];
         }
 #pragma unroll
         for (int q = 0; q < 6; ++q) rowf[q][tid] = f[q];
@@ -195,19 +208,17 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
     }
     // (visible to all after the first barrier below)
 
-    // acc <- (acc - mu_s u_s) * factor_s, per row (factor: rstd ratio, or rstd_2 at the end)
+    // Without split-K the accumulator carries sum_s rstd_s h_s . W'_s: at the
+    // end of state s (s < 2) it is scaled per row by rstd_s / rstd_{s+1}; the
+    // mean terms, sum_s rstd_s mu_s u_s, are subtracted in the epilogue.
     auto rescale = [&](int s) __attribute__((always_inline)) {
-        float uc[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) uc[j] = colf[s][wn * 128 + 16 * j + cb];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int r = wm * 128 + 16 * i + 4 * g + e;
-                const float mu = rowf[2 * s][r], fac = rowf[2 * s + 1][r];
+                const float fac = rowf[s][wm * 128 + 16 * i + 4 * g + e];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j][e] = (acc[i][j][e] - mu * uc[j]) * fac;
+                for (int j = 0; j < 8; ++j) acc[i][j][e] *= fac;
             }
         }
     };
@@ -341,9 +352,6 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
             }
         }
         if (tid == 0) a.counters[tile] = 0;
-    } else {
-        // last state: acc <- (acc - mu_2 u_2) * rstd_2
-        if (NORM != NORM_NONE) rescale(2);
     }
 
     // + c, round to bf16 and store.  Lane (g, cb) holds rows 4 g + e (e < 4)
@@ -357,16 +365,37 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
         const int rl = ((t & 1) << 1) | (t >> 1);
         auto swap1 = [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)); };
         auto swap2 = [](uint32_t x) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false); };
-        float cc[8];
+        // y = acc rstd_2 - sum_s (rstd_s mu_s) u_s + c (split-K: the reduction
+        // already applied the statistics, y = acc + c)
+        float cc[8], uu[3][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) cc[j] = colf[3][wn * 128 + 16 * j + cb];
+        for (int j = 0; j < 8; ++j) {
+            const int col = wn * 128 + 16 * j + cb;
+            cc[j] = colf[3][col];
+#pragma unroll
+            for (int q = 0; q < 3; ++q) uu[q][j] = (!SPLIT && NORM == NORM_LN) ? colf[q][col] : 0.f;
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int m = m0 + wm * 128 + 16 * i + 4 * g + rl;
+            float r2[4], rm[3][4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = wm * 128 + 16 * i + 4 * g + e;
+                r2[e] = (!SPLIT && NORM != NORM_NONE) ? rowf[2][rr] : 1.f;
+#pragma unroll
+                for (int q = 0; q < 3; ++q) rm[q][e] = (!SPLIT && NORM == NORM_LN) ? rowf[3 + q][rr] : 0.f;
+            }
+            auto fin = [&](float x, int j, int e) __attribute__((always_inline)) {
+                float y = x * r2[e] + cc[j];
+                if (!SPLIT && NORM == NORM_LN)
+                    y -= rm[0][e] * uu[0][j] + rm[1][e] * uu[1][j] + rm[2][e] * uu[2][j];
+                return y;
+            };
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float v0 = acc[i][j][0] + cc[j], v1 = acc[i][j][1] + cc[j];
-                const float v2 = acc[i][j][2] + cc[j], v3 = acc[i][j][3] + cc[j];
+                const float v0 = fin(acc[i][j][0], j, 0), v1 = fin(acc[i][j][1], j, 1);
+                const float v2 = fin(acc[i][j][2], j, 2), v3 = fin(acc[i][j][3], j, 3);
                 // even lanes keep rows 0, 1 and odd lanes rows 2, 3 of the pair's two columns
                 const float r0 = swap1(odd ? v0 : v2), r1 = swap1(odd ? v1 : v3);
                 const uint32_t P0 = odd ? pack_bf2(r0, v2) : pack_bf2(v0, r0);
