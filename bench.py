@@ -56,6 +56,30 @@ def parse():
     return p.parse_args()
 
 
+def measured_traffic(M):
+    """HBM bytes per launch of the decode kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, calibrated), or None when that
+    summary is for another token count or the kernel's sources have changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "gemv_split_d4096_M64_layernorm.md")
+    if M != 64 or not os.path.exists(path):
+        return None
+    rec = None
+    for line in open(path):
+        if line.startswith("TRAFFIC_JSON "):
+            rec = json.loads(line[len("TRAFFIC_JSON "):])
+    if rec is None:
+        return None
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for src in rec["sources"]:
+        with open(os.path.join(root, src), "rb") as f:
+            h.update(f.read())
+    return rec["traffic_bytes"] if h.hexdigest() == rec["sha256"] else None
+
+
 def alg_bytes(d, M, norm, has_beta, has_bias):
     """W + three hidden states + out + bf16 parameter vectors, each once."""
     nvec = 0
@@ -283,7 +307,7 @@ def main():
         print(json.dumps(copy_leg(torch)))
         return
     if args.only == "prefill":
-        print(json.dumps(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, max(3, args.steps), args.warmup)))
+        print(json.dumps(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, max(3, args.steps), args.warmup, folded=True)))
         return
     if args.only == "rowstats":
         inp = synth.make_inputs(4, with_weights=False)
@@ -309,12 +333,14 @@ def main():
     dec = decode_leg(torch, pkg, synth, args.M, args.steps, args.warmup, entry="folded")
 
     value = args.M * dec["steps"] / dec["seconds"]
-    kern_us = dec["event_us_mean"]
+    # one launch per call: HIP events around the timed region / launches
+    kern_us = dec["seconds"] / dec["steps"] * 1e6
     achieved = dec["bytes"] / (kern_us * 1e-6) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(args.M),
                     kernel="gemv_split_kernel (eagle31_fuse_folded, M<=64)",
-                    bytes_per_launch=dec["bytes"], launch_us_mean=round(kern_us, 3))
+                    bytes_per_launch=dec["bytes"], launch_us_mean=round(kern_us, 3),
+                    launch_us_mean_single_events=round(dec["event_us_mean"], 3))
 
     sweep = []
     if not args.no_sweep:
