@@ -55,6 +55,21 @@ constexpr int GV_WAVES = 8;          // waves per workgroup, at most
 constexpr int GV_THREADS = 64 * GV_WAVES;
 constexpr uint32_t BF16_ONE2 = 0x3F803F80u;  // two bfloat16 ones
 
+// 16-byte accesses to the split-K partials at the device coherence point
+// (buffer instructions with agent scope, sc1): the partials of one column
+// group are written by workgroups on other XCDs, whose L2s are not
+// coherent with this one.  The resource covers [base, base + bytes); an
+// access outside it reads 0 / is dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const float* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void store_coherent16(__amdgpu_buffer_rsrc_t rs, int off, const u32x4& v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 16);
+}
+__device__ __forceinline__ u32x4 load_coherent16(__amdgpu_buffer_rsrc_t rs, int off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 16);
+}
+
 // Coalesced load of a 16-row A tile: lane l reads row l / 4, 16-byte chunk
 // coal_chunk(l) of the 64-byte k-step; it lands in LDS slot l.
 __device__ __forceinline__ int coal_chunk(int lane) { return (lane & 3) ^ ((lane >> 4) & 3); }
@@ -394,10 +409,15 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
     }
     __syncthreads();
 
+    // the tile's first M rows go to this chunk's slot with 16-byte stores at
+    // the device coherence point (buffer stores with agent scope, sc1)
     const size_t slot = (size_t)grp * nchunks + ch;
-    float* part = a.part + slot * (size_t)ROWS * NCOL;
     const int nthreads = 64 * NW;
-    for (int v = tid; v < M * NCOL; v += nthreads) store_coherent(part + v, rowmaj[v]);
+    {
+        const __amdgpu_buffer_rsrc_t rs = part_rsrc(a.part + slot * (size_t)ROWS * NCOL, ROWS * NCOL * 4);
+        const u32x4* src4 = reinterpret_cast<const u32x4*>(rowmaj);
+        for (int v = tid; v < M * NCOL / 4; v += nthreads) store_coherent16(rs, v * 16, src4[v]);
+    }
 
     // Publish: every wave waits until its coherent stores have completed
     // (the workgroup barrier alone does not wait for them), then thread 0
@@ -417,44 +437,52 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
     if (NORM != NORM_NONE && wave == 0) stats_gather<NORM>(a, lane, sh_row);
     __syncthreads();
 
-    // outputs: thread -> column nl, rows rg, rg + rstep, ... in batches of
-    // 8; every partial load of a chunk round is issued before the first is used
+    // outputs: thread -> 4 consecutive columns (c4), rows rg, rg + rstep, ...
+    // Each pass covers 4 rows x 3 states x 2 chunks: its 24 16-byte loads are
+    // all issued before the first is used.  Chunks are summed in their order.
     const int kps = a.kps;
-    const int nl = tid % NCOL, rg = tid / NCOL, rstep = nthreads / NCOL;
-    const int n = grp * NCOL + nl;
-    float us[3] = {0.f, 0.f, 0.f};
-    if (NORM == NORM_LN)
+    constexpr int CQ = NCOL / 4;
+    const int c4 = tid % CQ, rg = tid / CQ, rstep = nthreads / CQ;
+    const int n = grp * NCOL + 4 * c4;
+    float us[3][4], cn[4];
 #pragma unroll
-        for (int ss = 0; ss < 3; ++ss) us[ss] = a.u[(size_t)ss * d + n];
-    const float cn = a.c[n];
-    const float* pbase = a.part + (size_t)grp * nchunks * ROWS * NCOL + nl;
+    for (int e = 0; e < 4; ++e) {
+        cn[e] = a.c[n + e];
+#pragma unroll
+        for (int ss = 0; ss < 3; ++ss) us[ss][e] = NORM == NORM_LN ? a.u[(size_t)ss * d + n + e] : 0.f;
+    }
+    const __amdgpu_buffer_rsrc_t rg_rs = part_rsrc(a.part + (size_t)grp * nchunks * ROWS * NCOL, nchunks * ROWS * NCOL * 4);
     if (rg < rstep) {
-        for (int m0 = rg; m0 < M; m0 += 8 * rstep) {
-            float ps[8][3];
+        for (int m0 = rg; m0 < M; m0 += 4 * rstep) {
+            f32x4 ps[4][3];
 #pragma unroll
-            for (int i8 = 0; i8 < 8; ++i8)
+            for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
-                for (int ss = 0; ss < 3; ++ss) ps[i8][ss] = 0.f;
-            for (int qq = 0; qq < kps; ++qq) {
-                float v[8][3];
+                for (int ss = 0; ss < 3; ++ss) ps[r4][ss] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int qq = 0; qq < kps; qq += 2) {
+                u32x4 v[4][3][2];
 #pragma unroll
-                for (int i8 = 0; i8 < 8; ++i8) {
-                    const int m = m0 + rstep * i8;
+                for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
                     for (int ss = 0; ss < 3; ++ss)
-                        v[i8][ss] = m < M ? load_coherent(pbase + (size_t)(ss * kps + qq) * ROWS * NCOL + (size_t)m * NCOL)
-                                          : 0.f;
-                }
 #pragma unroll
-                for (int i8 = 0; i8 < 8; ++i8)
+                        for (int q2 = 0; q2 < 2; ++q2) {
+                            const int m = m0 + rstep * r4;
+                            const int off = (((ss * kps + qq + q2) * ROWS + m) * NCOL + 4 * c4) * 4;
+                            v[r4][ss][q2] = (m < M && qq + q2 < kps) ? load_coherent16(rg_rs, off) : u32x4{0u, 0u, 0u, 0u};
+                        }
 #pragma unroll
-                    for (int ss = 0; ss < 3; ++ss) ps[i8][ss] += v[i8][ss];
+                for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+                    for (int ss = 0; ss < 3; ++ss)
+#pragma unroll
+                        for (int q2 = 0; q2 < 2; ++q2) ps[r4][ss] += __builtin_bit_cast(f32x4, v[r4][ss][q2]);
             }
 #pragma unroll
-            for (int i8 = 0; i8 < 8; ++i8) {
-                const int m = m0 + rstep * i8;
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int m = m0 + rstep * r4;
                 if (m >= M) continue;
-                float y = cn;
+                float y[4] = {cn[0], cn[1], cn[2], cn[3]};
 #pragma unroll
                 for (int ss = 0; ss < 3; ++ss) {
                     float mu = 0.f, r = 1.f;
@@ -462,11 +490,15 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
                         const float st[3] = {sh_row[ss * M + m][0], sh_row[ss * M + m][1], sh_row[ss * M + m][2]};
                         row_norm<NORM>(st, d, a.eps, mu, r);
                     }
-                    float pv = ps[i8][ss];
-                    if (NORM == NORM_LN) pv -= mu * us[ss];
-                    y += (NORM == NORM_NONE) ? pv : r * pv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        float pv = ps[r4][ss][e];
+                        if (NORM == NORM_LN) pv -= mu * us[ss][e];
+                        y[e] += (NORM == NORM_NONE) ? pv : r * pv;
+                    }
                 }
-                a.out[(size_t)m * d + n] = __builtin_bit_cast(uint16_t, (__bf16)y);
+                const uint2 w = make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
+                *reinterpret_cast<uint2*>(a.out + (size_t)m * d + n) = w;
             }
         }
     }
