@@ -263,8 +263,7 @@ template <int NORM, int MT, int NB, int R, int RA>
 __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
     constexpr int ROWS = 16 * MT;
     constexpr int NCOL = 16 * NB;            // columns per workgroup
-    constexpr int HB = NB / 2;               // column blocks per reduction half
-    constexpr int HALF_F4 = HB * MT * 64;    // f32x4 of half a wave tile
+    constexpr int TILE_F4 = NB * MT * 64;    // f32x4 of a wave tile
     const int M = a.M, d = a.d;
     const int ngroups = d / NCOL;
     const int nchunks = 3 * a.kps;
@@ -329,7 +328,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
     // LDS: during the loop the waves' A transpose tiles, afterwards the
     // pairwise-reduction buffers, then the row-major tile
     constexpr int LDS_A = GV_WAVES * MT * 64 * 16;
-    constexpr int LDS_RED = (GV_WAVES / 2) * HALF_F4 * 16;
+    constexpr int LDS_RED = (GV_WAVES / 2) * TILE_F4 * 16;  // at most 4 x 32 KiB
     constexpr int LDS_ROW = ROWS * NCOL * 4;
     constexpr int LDS_BYTES = LDS_A > LDS_RED ? (LDS_A > LDS_ROW ? LDS_A : LDS_ROW) : (LDS_RED > LDS_ROW ? LDS_RED : LDS_ROW);
     __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
@@ -374,28 +373,23 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
     __syncthreads();  // every wave is done with its A tile area
 
     // ---- pairwise sum of the wave tiles, e.g. for 8 waves
-    //      ((w0+w4)+(w2+w6))+((w1+w5)+(w3+w7)), half the column blocks at a time
+    //      ((w0+w4)+(w2+w6))+((w1+w5)+(w3+w7)): whole tiles, one round per level
     f32x4* buf = reinterpret_cast<f32x4*>(smem);
+    for (int half = NW / 2; half >= 1; half >>= 1) {
+        if (wave >= half && wave < 2 * half) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        for (int half = NW / 2; half >= 1; half >>= 1) {
-            if (wave >= half && wave < 2 * half) {
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int b = 0; b < HB; ++b)
-#pragma unroll
-                    for (int tt = 0; tt < MT; ++tt)
-                        buf[(wave - half) * HALF_F4 + (b * MT + tt) * 64 + lane] = acc[h * HB + b][tt];
-            }
-            __syncthreads();
-            if (wave < half) {
-#pragma unroll
-                for (int b = 0; b < HB; ++b)
-#pragma unroll
-                    for (int tt = 0; tt < MT; ++tt)
-                        acc[h * HB + b][tt] += buf[wave * HALF_F4 + (b * MT + tt) * 64 + lane];
-            }
-            __syncthreads();
+                for (int tt = 0; tt < MT; ++tt) buf[(wave - half) * TILE_F4 + (b * MT + tt) * 64 + lane] = acc[b][tt];
         }
+        __syncthreads();
+        if (wave < half) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int tt = 0; tt < MT; ++tt) acc[b][tt] += buf[wave * TILE_F4 + (b * MT + tt) * 64 + lane];
+        }
+        __syncthreads();
     }
     // wave 0 lays the tile out row-major [ROWS][NCOL] for coalesced stores
     float* rowmaj = reinterpret_cast<float*>(smem);
@@ -419,6 +413,12 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
         for (int v = tid; v < M * NCOL / 4; v += nthreads) store_coherent16(rs, v * 16, src4[v]);
     }
 
+    // Wave 0 gathers the statistics records now (every workgroup; they were
+    // published long before), so their loads share the round trip of the
+    // partial stores and the last arriver does not wait for them.
+    __shared__ float sh_row[3 * DECODE_MAX_M][3];  // (K, S1, S2) of row s M + m
+    if (NORM != NORM_NONE && wave == 0) stats_gather<NORM>(a, lane, sh_row);
+
     // Publish: every wave waits until its coherent stores have completed
     // (the workgroup barrier alone does not wait for them), then thread 0
     // counts the workgroup in.
@@ -433,10 +433,6 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
     if (!sh_last) return;
 
     // ================= last arriver of column group grp =================
-    __shared__ float sh_row[3 * DECODE_MAX_M][3];  // (K, S1, S2) of row s M + m
-    if (NORM != NORM_NONE && wave == 0) stats_gather<NORM>(a, lane, sh_row);
-    __syncthreads();
-
     // outputs: thread -> 4 consecutive columns (c4), rows rg, rg + rstep, ...
     // Each pass covers 4 rows x 3 states x 2 chunks: its 24 16-byte loads are
     // all issued before the first is used.  Chunks are summed in their order.
@@ -444,6 +440,20 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
     constexpr int CQ = NCOL / 4;
     const int c4 = tid % CQ, rg = tid / CQ, rstep = nthreads / CQ;
     const int n = grp * NCOL + 4 * c4;
+    const __amdgpu_buffer_rsrc_t rg_rs = part_rsrc(a.part + (size_t)grp * nchunks * ROWS * NCOL, nchunks * ROWS * NCOL * 4);
+    auto load_pass = [&](int m0, int qq, u32x4 (&v)[4][3][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+            for (int ss = 0; ss < 3; ++ss)
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2) {
+                    const int m = m0 + rstep * r4;
+                    const int off = (((ss * kps + qq + q2) * ROWS + m) * NCOL + 4 * c4) * 4;
+                    v[r4][ss][q2] = (m < M && qq + q2 < kps) ? load_coherent16(rg_rs, off) : u32x4{0u, 0u, 0u, 0u};
+                }
+    };
+
     float us[3][4], cn[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -451,7 +461,6 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
 #pragma unroll
         for (int ss = 0; ss < 3; ++ss) us[ss][e] = NORM == NORM_LN ? a.u[(size_t)ss * d + n + e] : 0.f;
     }
-    const __amdgpu_buffer_rsrc_t rg_rs = part_rsrc(a.part + (size_t)grp * nchunks * ROWS * NCOL, nchunks * ROWS * NCOL * 4);
     if (rg < rstep) {
         for (int m0 = rg; m0 < M; m0 += 4 * rstep) {
             f32x4 ps[4][3];
@@ -461,16 +470,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
                 for (int ss = 0; ss < 3; ++ss) ps[r4][ss] = f32x4{0.f, 0.f, 0.f, 0.f};
             for (int qq = 0; qq < kps; qq += 2) {
                 u32x4 v[4][3][2];
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4)
-#pragma unroll
-                    for (int ss = 0; ss < 3; ++ss)
-#pragma unroll
-                        for (int q2 = 0; q2 < 2; ++q2) {
-                            const int m = m0 + rstep * r4;
-                            const int off = (((ss * kps + qq + q2) * ROWS + m) * NCOL + 4 * c4) * 4;
-                            v[r4][ss][q2] = (m < M && qq + q2 < kps) ? load_coherent16(rg_rs, off) : u32x4{0u, 0u, 0u, 0u};
-                        }
+                load_pass(m0, qq, v);
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4)
 #pragma unroll
