@@ -136,6 +136,28 @@ def test_cfg4_long_prefill_sampled():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("folded", [False, True])
+def test_prefill_state_restart_ragged(folded):
+    """Prefill without split-K at a width whose state length is not a whole
+    number of pipeline cycles (d = 4160: 130 sub-tiles of 32 per state), so
+    the pipeline restarts at every state; M = 3100 leaves a ragged last
+    M-tile.  Sampled rows plus every row of the ragged tile."""
+    note(f"prefill restart d=4160 M=3100 folded={folded}")
+    d, M = 4160, 3100
+    w = synth.gen.custom_workload(d, (M,), seed_tag=4160)
+    inp = synth.make_inputs(w, M)
+    dv = DevInputs(inp)
+    if folded:
+        wf, u, c = e31().fold_prepare(LN, dv.gamma, dv.beta, dv.W, dv.bias)
+        G = bf16_to_f64(e31().fuse_folded(dv.h[0], dv.h[1], dv.h[2], LN, 1e-5, wf, u, c))
+    else:
+        G = run_fuse(dv, LN, 1e-5)
+    rows = np.unique(np.concatenate([sample_rows(M, 24, seed=41), np.arange(3072, M)]))
+    assert_parity(G[rows], oracle_rows(inp, LN, 1e-5, rows=rows), f"prefill restart folded={folded}")
+    del dv
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------ the fold path
 @pytest.mark.parametrize("cfg,kind,eps", [(1, LN, 1e-5), (3, RMS, 1e-6), (1, NONE, 0.0)])
 def test_fold_prepare_exact_weight_and_vectors(cfg, kind, eps):
