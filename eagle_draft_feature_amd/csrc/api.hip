@@ -252,7 +252,6 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
 
     // prefill: statistics, (fold the stored W), GEMM
     const PrefillPlan p = plan_prefill((int)M, (int)d);
-    if (p.splits > 1 && p.tiles_m * p.tiles_n > MAX_COUNTERS) return EAGLE31_ERR_SHAPE;
     float* mu = at<float>(ws, L.mu);
     float* rstd = at<float>(ws, L.rstd);
     if (norm != NORM_NONE) {
@@ -282,7 +281,6 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
     a.d = (int)d;
     a.norm = norm;
     a.splits = p.splits;
-    a.counters = at<int>(ws, L.counters);
     a.part = at<float>(ws, L.part);
     e = launch_prefill(a, p, st);
     if (e != hipSuccess) return hip_fail(e);

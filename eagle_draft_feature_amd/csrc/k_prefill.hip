@@ -26,8 +26,9 @@
 // of 4 M-tiles, and consecutive workgroup ids are spread so that each XCD
 // (workgroup id mod 8) takes a contiguous run of that order: the tiles an
 // XCD runs at once share A and B tiles in its L2.
-// Few tiles (small M) split K by chunks that never cross a state; partials go
-// to a workspace and the last workgroup of a tile sums them in a fixed order.
+// Few tiles (small M) split K by chunks that never cross a state; the chunks'
+// partials go to the workspace and a reduction kernel launched next on the
+// stream sums them in a fixed order and applies the statistics.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -64,6 +65,32 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// Stores one lane's part of a 16 x 16 fp32 block as bf16.  Lane (g, cb) holds
+// rows row0 + e (e < 4; row0 = block row + 4 g) of column col0 + cb.  Two
+// exchanges inside each quad of lanes (cb = 4 k + t; partners t ^ 1, then
+// t ^ 2) leave lane t with one row, row0 + (((t & 1) << 1) | (t >> 1)), and
+// the quad's 4 columns col0 + 4 k .. + 3: one 8-byte store, no staging
+// through LDS.  Rows from M and columns from d on are not stored.
+__device__ __forceinline__ void store_block_bf16(uint16_t* out, int M, int d, int row0, int col0, int cb, float v0,
+                                                 float v1, float v2, float v3) {
+    const int t = cb & 3, k4 = cb >> 2;
+    const bool odd = (t & 1) != 0, hi = t >= 2;
+    auto swap1 = [](float x) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+    };
+    auto swap2 = [](uint32_t x) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false); };
+    // even lanes keep rows 0, 1 and odd lanes rows 2, 3 of the pair's two columns
+    const float r0 = swap1(odd ? v0 : v2), r1 = swap1(odd ? v1 : v3);
+    const uint32_t P0 = odd ? pack_bf2(r0, v2) : pack_bf2(v0, r0);
+    const uint32_t P1 = odd ? pack_bf2(r1, v3) : pack_bf2(v1, r1);
+    // then each lane keeps one row of the quad's four columns
+    const uint32_t rv = swap2(hi ? P0 : P1);
+    const uint2 w = hi ? make_uint2(rv, P1) : make_uint2(P0, rv);
+    const int m = row0 + (((t & 1) << 1) | (t >> 1));
+    const int n = col0 + 4 * k4;
+    if (m < M && n < d) *reinterpret_cast<uint2*>(out + (size_t)m * d + n) = w;
+}
 
 struct TileCoord {
     int mt, nt, chunk, gsz;  // gsz: M-tiles in the raster group of the tile
@@ -304,110 +331,104 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
     __builtin_amdgcn_s_waitcnt(0);
 
     if (SPLIT) {
-        // partial of this chunk in fragment order, then the last arriver sums
-        const int splits = a.splits;
+        // this chunk's partial in fragment order; the reduction kernel that
+        // runs next on the stream sums the chunks (rows from M on are skipped)
         const int tile = tc.mt * TN + tc.nt;
         const size_t frag_per_wg = (size_t)PTH * 64;  // f32x4 per (tile, chunk)
-        f32x4* part = reinterpret_cast<f32x4*>(a.part);
-        f32x4* mine = part + ((size_t)tile * splits + tc.chunk) * frag_per_wg;
+        f32x4* mine = reinterpret_cast<f32x4*>(a.part) + ((size_t)tile * a.splits + tc.chunk) * frag_per_wg;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             if (m0 + wm * 128 + 16 * i >= M) continue;
 #pragma unroll
             for (int j = 0; j < 8; ++j) mine[((size_t)(i * 8 + j) * 4 + wave) * 64 + lane] = acc[i][j];
         }
-        __threadfence();
-        __syncthreads();
-        __shared__ int sh_last;
-        if (tid == 0) {
-            const int old = __hip_atomic_fetch_add(a.counters + tile, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-            sh_last = (old == splits - 1);
-        }
-        __syncthreads();
-        if (!sh_last) return;
-        __threadfence();
-        const int kps = splits / 3;
-        // fragment by fragment: y = sum_s rstd_s * (sum_{chunks of s} P - mu_s u_s)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                f32x4 y = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (m0 + wm * 128 + 16 * i < M) {
-                    for (int s = 0; s < 3; ++s) {
-                        f32x4 ss = f32x4{0.f, 0.f, 0.f, 0.f};
-                        for (int ch = s * kps; ch < (s + 1) * kps; ++ch)
-                            ss += part[((size_t)tile * splits + ch) * frag_per_wg + ((size_t)(i * 8 + j) * 4 + wave) * 64 +
-                                       lane];
-                        const float uc = colf[s][wn * 128 + 16 * j + cb];
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int rr = wm * 128 + 16 * i + 4 * g + e;
-                            const float mu = rowf[2 * s][rr], r = rowf[2 * s + 1][rr];
-                            y[e] += (ss[e] - mu * uc) * r;
-                        }
-                    }
-                }
-                acc[i][j] = y;
-            }
-        }
-        if (tid == 0) a.counters[tile] = 0;
+        return;
     }
 
-    // + c, round to bf16 and store.  Lane (g, cb) holds rows 4 g + e (e < 4)
-    // of column cb of each 16 x 16 block.  Two exchanges inside each quad of
-    // lanes (cb = 4 k + t; partners t ^ 1, then t ^ 2) leave lane t with one
-    // row, ((t & 1) << 1) | (t >> 1), and the quad's 4 columns 4 k .. 4 k + 3:
-    // one 8-byte store, no staging through LDS.
-    {
-        const int t = cb & 3, k4 = cb >> 2;
-        const bool odd = (t & 1) != 0, hi = t >= 2;
-        const int rl = ((t & 1) << 1) | (t >> 1);
-        auto swap1 = [](float x) { return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false)); };
-        auto swap2 = [](uint32_t x) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false); };
-        // y = acc rstd_2 - sum_s (rstd_s mu_s) u_s + c (split-K: the reduction
-        // already applied the statistics, y = acc + c)
-        float cc[8], uu[3][8];
+    // y = acc rstd_2 - sum_s (rstd_s mu_s) u_s + c, rounded to bf16
+    float cc[8], uu[3][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int col = wn * 128 + 16 * j + cb;
-            cc[j] = colf[3][col];
+    for (int j = 0; j < 8; ++j) {
+        const int col = wn * 128 + 16 * j + cb;
+        cc[j] = colf[3][col];
 #pragma unroll
-            for (int q = 0; q < 3; ++q) uu[q][j] = (!SPLIT && NORM == NORM_LN) ? colf[q][col] : 0.f;
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int m = m0 + wm * 128 + 16 * i + 4 * g + rl;
-            float r2[4], rm[3][4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int rr = wm * 128 + 16 * i + 4 * g + e;
-                r2[e] = (!SPLIT && NORM != NORM_NONE) ? rowf[2][rr] : 1.f;
-#pragma unroll
-                for (int q = 0; q < 3; ++q) rm[q][e] = (!SPLIT && NORM == NORM_LN) ? rowf[3 + q][rr] : 0.f;
-            }
-            auto fin = [&](float x, int j, int e) __attribute__((always_inline)) {
-                float y = x * r2[e] + cc[j];
-                if (!SPLIT && NORM == NORM_LN)
-                    y -= rm[0][e] * uu[0][j] + rm[1][e] * uu[1][j] + rm[2][e] * uu[2][j];
-                return y;
-            };
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float v0 = fin(acc[i][j][0], j, 0), v1 = fin(acc[i][j][1], j, 1);
-                const float v2 = fin(acc[i][j][2], j, 2), v3 = fin(acc[i][j][3], j, 3);
-                // even lanes keep rows 0, 1 and odd lanes rows 2, 3 of the pair's two columns
-                const float r0 = swap1(odd ? v0 : v2), r1 = swap1(odd ? v1 : v3);
-                const uint32_t P0 = odd ? pack_bf2(r0, v2) : pack_bf2(v0, r0);
-                const uint32_t P1 = odd ? pack_bf2(r1, v3) : pack_bf2(v1, r1);
-                // then each lane keeps one row of the quad's four columns
-                const uint32_t rv = swap2(hi ? P0 : P1);
-                const uint2 w = hi ? make_uint2(rv, P1) : make_uint2(P0, rv);
-                const int n = n0 + wn * 128 + 16 * j + 4 * k4;
-                if (m < M && n < d) *reinterpret_cast<uint2*>(a.out + (size_t)m * d + n) = w;
-            }
-        }
+        for (int q = 0; q < 3; ++q) uu[q][j] = NORM == NORM_LN ? colf[q][col] : 0.f;
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float r2[4], rm[3][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int rr = wm * 128 + 16 * i + 4 * g + e;
+            r2[e] = NORM != NORM_NONE ? rowf[2][rr] : 1.f;
+#pragma unroll
+            for (int q = 0; q < 3; ++q) rm[q][e] = NORM == NORM_LN ? rowf[3 + q][rr] : 0.f;
+        }
+        auto fin = [&](float x, int j, int e) __attribute__((always_inline)) {
+            float y = x * r2[e] + cc[j];
+            if (NORM == NORM_LN) y -= rm[0][e] * uu[0][j] + rm[1][e] * uu[1][j] + rm[2][e] * uu[2][j];
+            return y;
+        };
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            store_block_bf16(a.out, M, d, m0 + wm * 128 + 16 * i + 4 * g, n0 + wn * 128 + 16 * j, cb,
+                             fin(acc[i][j][0], j, 0), fin(acc[i][j][1], j, 1), fin(acc[i][j][2], j, 2),
+                             fin(acc[i][j][3], j, 3));
+    }
+}
+
+// Split-K reduction: one wave per fragment group (tile, i, j, wave of the
+// main kernel), whose 64 lanes hold the same rows and columns as in the main
+// kernel.  y = sum_s rstd_s (sum over the chunks of state s, in their order,
+// - mu_s u_s) + c, stored through the same quad exchange.  It runs after the
+// main kernel on the stream, so plain loads see the partials.
+template <int NORM>
+__global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillArgs a, int TM, int TN) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, cb = lane & 15;
+    const int fg = blockIdx.x * 4 + (threadIdx.x >> 6);  // 256 fragment groups per tile
+    const int tile = fg >> 8;
+    if (tile >= TM * TN) return;
+    const int ij = (fg >> 2) & 63, w = fg & 3;
+    const int i = ij >> 3, j = ij & 7, wm = w >> 1, wn = w & 1;
+    const int mt = tile / TN, nt = tile - mt * TN;
+    const int M = a.M, d = a.d;
+    const int row0 = mt * PBM + wm * 128 + 16 * i + 4 * g;
+    if (mt * PBM + wm * 128 + 16 * i >= M) return;  // whole wave: rows the main kernel did not store
+    const int col = nt * PBN + wn * 128 + 16 * j + cb;
+    const int splits = a.splits, kps = splits / 3;
+    const f32x4* part = reinterpret_cast<const f32x4*>(a.part) + (size_t)tile * splits * PTH * 64 + (size_t)(ij * 4 + w) * 64 + lane;
+    f32x4 ps[3];
+#pragma unroll
+    for (int ss = 0; ss < 3; ++ss) {
+        f32x4 v[8];
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch)
+            v[ch] = ch < kps ? part[(size_t)(ss * kps + ch) * PTH * 64] : f32x4{0.f, 0.f, 0.f, 0.f};
+        ps[ss] = v[0];
+#pragma unroll
+        for (int ch = 1; ch < 8; ++ch)
+            if (ch < kps) ps[ss] += v[ch];
+    }
+    const bool colok = col < d;
+    const float cn = colok ? a.c[col] : 0.f;
+    float uc[3] = {0.f, 0.f, 0.f};
+    if (NORM == NORM_LN && colok)
+#pragma unroll
+        for (int ss = 0; ss < 3; ++ss) uc[ss] = a.u[(size_t)ss * d + col];
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int m = min(row0 + e, M - 1);
+        float acc = cn;
+#pragma unroll
+        for (int ss = 0; ss < 3; ++ss) {
+            float pv = ps[ss][e];
+            if (NORM == NORM_LN) pv -= a.mu[(size_t)ss * M + m] * uc[ss];
+            acc += NORM == NORM_NONE ? pv : a.rstd[(size_t)ss * M + m] * pv;
+        }
+        y[e] = acc;
+    }
+    store_block_bf16(a.out, M, d, row0, nt * PBN + wn * 128 + 16 * j, cb, y[0], y[1], y[2], y[3]);
 }
 
 PrefillPlan plan_prefill(int M, int d) {
@@ -423,10 +444,7 @@ PrefillPlan plan_prefill(int M, int d) {
         while (tiles * 3 * kps < 256 && kps * 2 <= KTS && kps < 8) kps *= 2;
         p.splits = 3 * kps;
     }
-    if (p.splits > 1) {
-        p.counters_bytes = ((size_t)tiles * sizeof(int) + 255) / 256 * 256;
-        p.part_bytes = (size_t)tiles * p.splits * PTH * 64 * sizeof(f32x4);
-    }
+    if (p.splits > 1) p.part_bytes = (size_t)tiles * p.splits * PTH * 64 * sizeof(f32x4);
     return p;
 }
 
@@ -435,6 +453,12 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& p, h
     const int items = p.tiles_m * p.tiles_n * (SPLIT ? p.splits : 1);
     const int grid = ((items + 7) / 8) * 8;
     prefill_kernel<SPLIT, NORM><<<grid, PTH, 0, st>>>(a, p.tiles_m, p.tiles_n);
+    if (SPLIT) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        // 256 fragment groups per tile, 4 per workgroup
+        prefill_reduce_kernel<NORM><<<p.tiles_m * p.tiles_n * 64, 256, 0, st>>>(a, p.tiles_m, p.tiles_n);
+    }
     return hipGetLastError();
 }
 

@@ -87,7 +87,8 @@ hipError_t launch_fold_prepare(int d, int norm, const uint16_t* const gamma[3], 
 
 // ------------------------------------------------------------------ prefill
 // Large-M path: GEMM on raw hidden states and the folded weight tiles,
-// per-row rescale at the state boundaries (fold), optional split-K.
+// per-row rescale at the state boundaries (fold), optional split-K (the
+// chunks' partials are summed by a reduction kernel launched after it).
 struct PrefillArgs {
     const uint16_t* h[3];
     const uint16_t* wt;   // folded weight tiles
@@ -99,14 +100,13 @@ struct PrefillArgs {
     int M, d;
     int norm;
     int splits;           // 1 or a multiple of 3
-    int* counters;        // [tiles] for split-K
-    float* part;          // split partials
+    float* part;          // split-K partials (summed by a second kernel)
 };
 
 struct PrefillPlan {
     int splits = 1;
     int tiles_m = 0, tiles_n = 0;
-    size_t counters_bytes = 0, part_bytes = 0;
+    size_t part_bytes = 0;
 };
 
 PrefillPlan plan_prefill(int M, int d);
