@@ -215,7 +215,12 @@ def decode_leg(torch, pkg, synth, M, steps, warmup, entry="folded", repeats=5):
 
 
 def prefill_leg(torch, pkg, synth, cfg, M, kind, eps, steps, warmup, folded=False):
-    inp = cached_inputs(synth, cfg, M)
+    """One workload through eagle31_fuse (stored W) or eagle31_fuse_folded
+    (weight folded beforehand), cold-cache rotation; reports tokens/s and the
+    fraction of both peaks (HBM with the entry point's algorithmic bytes,
+    MFMA with 2 M 3d d flops)."""
+    # a smaller M is the prefix of the workload's largest M
+    inp = cached_inputs(synth, cfg, synth.CONFIGS[cfg].max_M).rows(M)
     foot = 3 * inp.d * inp.d * 2 + 4 * M * inp.d * 2
     R = 2 if foot >= MALL_BYTES else rotation_count(foot)
     rot = Rotation(inp, R, torch)
@@ -232,8 +237,12 @@ def prefill_leg(torch, pkg, synth, cfg, M, kind, eps, steps, warmup, folded=Fals
 
     t, _ = time_loop(torch, fn, R, steps, warmup)
     per = t / steps
-    res = dict(workload=synth.CONFIGS[cfg].name, d=inp.d, M=M, norm=kind, variant="folded" if folded else "plain",
+    nbytes = folded_bytes(inp.d, M) if folded else alg_bytes(inp.d, M, kind, inp.beta is not None,
+                                                              inp.bias is not None)
+    res = dict(workload=synth.CONFIGS[cfg].name, d=inp.d, M=M, norm=synth.workloads.NORM_NAMES[kind],
+               variant="folded" if folded else "plain", steps=steps,
                ms_per_step=per * 1e3, tokens_per_s=M / per,
+               hbm_frac=nbytes / per / 1e9 / HBM_PEAK_GBS,
                mfma_frac=flops(inp.d, M) / per / 1e12 / BF16_PEAK_TFLOPS,
                tflops=flops(inp.d, M) / per / 1e12)
     del rot
@@ -355,11 +364,21 @@ def main():
                                   event_us_mean=round(r["event_us_mean"], 3)))
 
     prefill = []
+    others = []
     if not args.no_prefill:
         prefill.append(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, 10, 3, folded=False))
         prefill.append(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, 10, 3, folded=True))
         prefill.append(prefill_leg(torch, pkg, synth, 5, 4096, 1, 1e-5, 30, 5, folded=False))
         prefill.append(prefill_leg(torch, pkg, synth, 5, 4096, 1, 1e-5, 30, 5, folded=True))
+        # the other sizes of the draft-tree and chunked-prefill workloads
+        # (reported against both peaks; the graded bars are the lines above)
+        for M in (64, 128, 256):
+            for folded in (True, False):
+                others.append(prefill_leg(torch, pkg, synth, 3, M, 2, 1e-6, 200, 20, folded=folded))
+        for kind, eps in ((1, 1e-5), (2, 1e-6)):
+            for M in (512, 2048, 4093) + ((4096,) if kind == 2 else ()):
+                others.append(prefill_leg(torch, pkg, synth, 5, M, kind, eps, 30 if M < 4000 else 20, 5,
+                                          folded=True))
 
     cpu = None
     if not args.no_cpu:
@@ -387,6 +406,7 @@ def main():
         "cpu_baseline": cpu,
         "decode_sweep": sweep,
         "prefill": prefill,
+        "other_workloads": others,
     }
     print(json.dumps(line))
 
