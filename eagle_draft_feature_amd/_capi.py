@@ -59,6 +59,7 @@ SIGNATURES = {
     "eagle31_status_string": (ctypes.c_char_p, [_int]),
     "eagle31_last_hip_error": (_int, []),
     "eagle31_release": (_int, []),
+    "eagle31_debug_stats_recompute": (_int, [_int]),
 }
 
 

@@ -173,6 +173,10 @@ int owned_workspace(size_t need, hipStream_t st, void** out_ptr, size_t* out_byt
 // Id stamped on the statistics records of one decode call: process-wide,
 // never 0 (a zeroed workspace holds no valid record), so a record left by an
 // earlier call on the same workspace never matches.
+// Set by eagle31_debug_stats_recompute: the folded decode kernel's readers
+// take their fallback path (recompute the statistics rows) at once.
+std::atomic<int> g_stats_recompute{0};
+
 uint32_t next_call_id() {
     static std::atomic<uint32_t> counter{0};
     uint32_t id;
@@ -221,6 +225,7 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
         a.part = at<float>(ws, L.part);
         a.rstats = at<uint32_t>(ws, L.stats);
         a.call_id = next_call_id();
+        a.stats_recompute = g_stats_recompute.load(std::memory_order_relaxed);
         e = launch_gemv(a, norm, p, st);
         if (e != hipSuccess) return hip_fail(e);
         return EAGLE31_OK;
@@ -349,6 +354,11 @@ size_t eagle31_workspace_size(int64_t M, int64_t d, int norm_kind) {
     const WsLayout a = layout_for(M, d, norm_kind, false);
     const WsLayout b = layout_for(M, d, norm_kind, true);
     return a.total > b.total ? a.total : b.total;
+}
+
+int eagle31_debug_stats_recompute(int on) {
+    g_stats_recompute.store(on ? 1 : 0, std::memory_order_relaxed);
+    return EAGLE31_OK;
 }
 
 int eagle31_workspace_init(void* workspace, size_t ws_bytes, void* stream) {

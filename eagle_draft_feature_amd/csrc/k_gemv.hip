@@ -187,7 +187,7 @@ __device__ void stats_gather(const GemvArgs& a, int lane, float (*out)[3]) {
     const int need = 3 * a.M;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     bool ready = false;
-    for (;;) {
+    for (; !a.stats_recompute;) {
         uint32_t f[MAXR / 64];
 #pragma unroll
         for (int j = 0; j < MAXR / 64; ++j) {

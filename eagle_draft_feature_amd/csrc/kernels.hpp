@@ -69,6 +69,7 @@ struct GemvArgs {
     float* part;          // [column groups * 3 kps * 16 MT * 16 nb]
     uint32_t* rstats;     // [3 M][4]: (K, S1, S2, call id) per (state, token) row
     uint32_t call_id;     // nonzero, different from the previous calls' on this workspace
+    int stats_recompute;  // nonzero: readers recompute the statistics instead of waiting for the records
 };
 
 struct GemvPlan {

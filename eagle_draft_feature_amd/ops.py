@@ -179,3 +179,9 @@ def row_stats(h_low, h_mid, h_high, norm, eps):
 
 def release() -> None:
     check("eagle31_release", lib().eagle31_release())
+
+
+def debug_stats_recompute(on: bool) -> None:
+    """Test hook: the folded decode kernel's statistics readers recompute the
+    rows instead of waiting for the published records (same result)."""
+    check("eagle31_debug_stats_recompute", lib().eagle31_debug_stats_recompute(1 if on else 0))

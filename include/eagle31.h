@@ -175,6 +175,18 @@ int eagle31_last_hip_error(void);
  * while work that uses it is still queued. */
 int eagle31_release(void);
 
+/*
+ * eagle31_debug_stats_recompute - test hook for the folded decode path
+ * (eagle31_fuse_folded with M <= 64).  That kernel computes each token's
+ * statistics once and hands them between workgroups through the workspace;
+ * a reader waits a bounded time for them and, if they are not there, computes
+ * the rows itself with the same arithmetic.  With on != 0 every reader takes
+ * that fallback at once, so a test can check that it gives the same bits.
+ * Process-wide; applies to calls enqueued after it returns; always returns
+ * EAGLE31_OK.  Slower, and never needed in production.
+ */
+int eagle31_debug_stats_recompute(int on);
+
 #ifdef __cplusplus
 }
 #endif

@@ -197,6 +197,33 @@ def test_fuse_folded_parity(cfg, M, kind, eps):
     assert_parity(G[rows], oracle_rows(sub, kind, eps, rows=rows), f"folded cfg{cfg} M={M}")
 
 
+@pytest.mark.parametrize("cfg,M,kind,eps", [(2, 1, LN, 1e-5), (2, 64, LN, 1e-5), (3, 64, RMS, 1e-6),
+                                            (1, 17, LN, 1e-5), (1, 64, NONE, 0.0)])
+def test_folded_stats_recompute_path_same_bits(cfg, M, kind, eps):
+    """The folded decode kernel hands each token's statistics between
+    workgroups; a reader that does not find them computes the rows itself.
+    Forced from the host, that fallback gives the same bits as the normal
+    path, and both match the oracle."""
+    note(f"stats recompute path cfg{cfg} M={M} kind={kind}")
+    inp = inputs(cfg, synth.CONFIGS[cfg].max_M if cfg != 2 else 64)
+    dv = DevInputs(inp)
+    wf, u, c = e31().fold_prepare(kind, dv.gamma, dv.beta, dv.W, dv.bias)
+    h = [x[:M] for x in dv.h]
+    normal = e31().fuse_folded(h[0], h[1], h[2], kind, eps, wf, u, c)
+    torch.cuda.synchronize()
+    e31().debug_stats_recompute(True)
+    try:
+        forced = e31().fuse_folded(h[0], h[1], h[2], kind, eps, wf, u, c)
+        torch.cuda.synchronize()
+    finally:
+        e31().debug_stats_recompute(False)
+    assert torch.equal(normal.view(torch.int16), forced.view(torch.int16)), "fallback statistics differ"
+    again = e31().fuse_folded(h[0], h[1], h[2], kind, eps, wf, u, c)
+    torch.cuda.synchronize()
+    assert torch.equal(normal.view(torch.int16), again.view(torch.int16))
+    assert_parity(bf16_to_f64(forced), oracle_rows(inp.rows(M), kind, eps), f"recompute cfg{cfg} M={M}")
+
+
 # ------------------------------------------------ properties and edge cases
 @pytest.mark.parametrize("cfg,M,kind", [(1, 64, LN), (2, 16, LN), (3, 64, RMS), (5, 512, LN)])
 def test_gpu_scale_invariance(cfg, M, kind):
