@@ -138,3 +138,13 @@ def test_python_wrapper_checks_types_without_gpu():
         e31.fuse(x, x, x, "ln", 1e-5, None, None, torch.zeros(384, 128, dtype=torch.bfloat16), None)
     with pytest.raises(TypeError):
         e31.fuse(x.float(), x, x, "ln", 1e-5, None, None, x, None)
+
+
+def test_stats_recompute_hook_is_host_only():
+    """The test hook only sets a process-wide flag read at the next launch:
+    it returns OK without touching the GPU, and can be switched back."""
+    L = e31.lib()
+    assert L.eagle31_debug_stats_recompute(1) == 0
+    assert L.eagle31_debug_stats_recompute(0) == 0
+    e31.debug_stats_recompute(True)
+    e31.debug_stats_recompute(False)
