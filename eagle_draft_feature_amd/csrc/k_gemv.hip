@@ -53,7 +53,6 @@ namespace e31 {
 
 constexpr int GV_WAVES = 8;          // waves per workgroup, at most
 constexpr int GV_THREADS = 64 * GV_WAVES;
-constexpr uint32_t BF16_ONE2 = 0x3F803F80u;  // two bfloat16 ones
 
 // 16-byte accesses to the split-K partials at the device coherence point
 // (buffer instructions with agent scope, sc1): the partials of one column

@@ -35,7 +35,6 @@
 namespace e31 {
 
 constexpr int PBM = 256, PBN = 256, PBK = 32, PTH = 256;  // PBK: k per sub-tile (one MFMA k-step)
-constexpr int NST = 4;   // LDS stages
 constexpr int PGM = 4;   // M-tiles per raster group
 constexpr int STAGE_A = PBM * PBK * 2;              // A part of a stage (16 KiB)
 constexpr int STAGE_BYTES = (PBM + PBN) * PBK * 2;  // A then B (32 KiB)
