@@ -298,9 +298,8 @@ def copy_leg(torch, nbytes=1 << 30, steps=20):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the fused step is row independent and this build runs on a "
-              "single MI355X (multi-GPU sharding is a design note, not measured). Use --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU: the fused step is row independent, and how it would shard over "
+              "several GPUs is described, not measured. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
 
