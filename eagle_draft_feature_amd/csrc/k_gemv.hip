@@ -504,12 +504,192 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
     if (tid == 0) __hip_atomic_store(a.counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// =====================================================================
+// One token: one 16-column block x the whole K per workgroup
+// =====================================================================
+//
+// With one token the hidden states are tiny (24 KiB at d = 4096), so every
+// workgroup copies them into LDS once, computes their statistics itself (the
+// same shifted sums as the split kernel's, from LDS), and walks the whole K
+// for one 16-column block of W': no split-K partials, no counters, nothing
+// handed between workgroups (d = 4096 gives 256 workgroups, one per CU).
+// Wave w of 16 takes the k-steps w, w + 16, ... of each state in turn, one
+// accumulator per state, with an R-step W' ring; the A fragment of a step is
+// one LDS read (token rows padded by 64 bytes, so that with several tokens the
+// distinct rows would fall in different banks).  The waves' per-state tiles
+// are summed in LDS in wave order, and wave 0 applies
+// sum_s rstd_s (P_s - mu_s u_s) + c.
+constexpr int WH_MAXM = 1;  // measured: from two tokens on the split kernel is as fast
+constexpr int WH_A_BYTES = WH_MAXM * (6 * 4096 + 64);  // token rows in LDS, at most
+constexpr int WH_WAVES = 16;
+
+template <int NORM, int R>
+__global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
+    __shared__ __attribute__((aligned(16))) char la[WH_A_BYTES];
+    __shared__ f32x4 red[WH_WAVES][3][64];
+    __shared__ float sst[3 * WH_MAXM][3];
+    const int M = a.M, d = a.d;
+    const int T3 = d >> 5, JS = T3 / WH_WAVES;  // k-steps per state and wave
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, cb = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = blockIdx.x;
+    if (grp >= (d >> 4)) return;
+    const int rstride = 6 * d + 64;
+
+    // W' tiles of column block grp: this wave's local step j is k-step wave + 8 j
+    const u32x4* __restrict__ wp = reinterpret_cast<const u32x4*>(a.wp) + ((size_t)grp * 3 * T3 + wave) * 64 + lane;
+    constexpr int WSTEP = WH_WAVES * 64;  // uint4 between a wave's steps
+    u32x4 rw[R];
+#pragma unroll
+    for (int p = 0; p < R; ++p) rw[p] = wp[(size_t)p * WSTEP];
+
+    // token rows into LDS, states concatenated (row m: k = 0 .. 3d-1)
+    {
+        const uint64_t hp0 = reinterpret_cast<uint64_t>(a.h[0]);
+        const uint64_t hd1 = reinterpret_cast<uint64_t>(a.h[1]) - hp0;
+        const uint64_t hd2 = reinterpret_cast<uint64_t>(a.h[2]) - hp0;
+        const int cpr = (3 * d) >> 3, cps = d >> 3;  // 16-byte chunks per row / per state
+        for (int v = tid; v < M * cpr; v += 64 * WH_WAVES) {
+            const int m = v / cpr, c = v - m * cpr;
+            const int st = (c >= cps) + (c >= 2 * cps);
+            const uint64_t base = hp0 + (uint64_t)(st == 1) * hd1 + (uint64_t)(st == 2) * hd2;
+            const uint16_t* src = reinterpret_cast<const uint16_t*>(base) + (size_t)m * d + 8 * (c - st * cps);
+            *reinterpret_cast<uint4*>(la + m * rstride + c * 16) = *reinterpret_cast<const uint4*>(src);
+        }
+    }
+    __syncthreads();
+
+    // statistics of the 3M (state, token) rows: wave w takes rows w, w + 8
+    if (NORM != NORM_NONE) {
+        for (int it = wave; it < 3 * M; it += WH_WAVES) {
+            const int st = it / M, m = it - st * M;
+            const char* row = la + m * rstride + st * d * 2;
+            float K = 0.f;
+            if (NORM == NORM_LN) {
+                const uint4 x = *reinterpret_cast<const uint4*>(row + 16 * (lane & 3));
+                float v = ((bf_lo(x.x) + bf_hi(x.x)) + (bf_lo(x.y) + bf_hi(x.y))) +
+                          ((bf_lo(x.z) + bf_hi(x.z)) + (bf_lo(x.w) + bf_hi(x.w)));
+                v += __shfl_xor(v, 1, 64);
+                v += __shfl_xor(v, 2, 64);
+                K = v * (1.0f / 32.0f);
+            }
+            float s1 = 0.f, s2 = 0.f;
+            for (int c = lane; c < (d >> 3); c += 64) {
+                const uint4 x = *reinterpret_cast<const uint4*>(row + 16 * c);
+                const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float x0 = bf_lo(w4[e]), x1 = bf_hi(w4[e]);
+                    if (NORM == NORM_LN) {
+                        x0 -= K;
+                        x1 -= K;
+                        s1 += x0 + x1;
+                    }
+                    s2 = fmaf(x0, x0, fmaf(x1, x1, s2));
+                }
+            }
+            const float S1 = wave_sum(s1), S2 = wave_sum(s2);
+            if (lane == 0) {
+                sst[it][0] = K;
+                sst[it][1] = S1;
+                sst[it][2] = S2;
+            }
+        }
+    }
+
+    // MFMA lane L: token row L % 16 (clamped to M - 1), 16-byte chunk L / 16 of the step
+    const char* abase = la + min(cb, M - 1) * rstride + 16 * g;
+    f32x4 acc[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // one state: its ring blocks refill R steps ahead (the last block of the
+    // last state does not); slot = local step % R, static
+    auto run_state = [&](f32x4& ac, int j0, bool last) __attribute__((always_inline)) {
+        int i = 0;
+        const int nfull = last ? JS - R : JS;
+        for (; i < nfull; i += R) {
+#pragma unroll
+            for (int p = 0; p < R; ++p) {
+                const int jj = j0 + i + p;
+                const u32x4 af = *reinterpret_cast<const u32x4*>(abase + (wave + WH_WAVES * jj) * 64);
+                ac = mfma16x16x32(af, rw[p], ac);
+                rw[p] = wp[(size_t)(jj + R) * WSTEP];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (last) {
+#pragma unroll
+            for (int p = 0; p < R; ++p) {
+                const int jj = j0 + i + p;
+                const u32x4 af = *reinterpret_cast<const u32x4*>(abase + (wave + WH_WAVES * jj) * 64);
+                ac = mfma16x16x32(af, rw[p], ac);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    run_state(acc[0], 0, false);
+    run_state(acc[1], JS, false);
+    run_state(acc[2], 2 * JS, true);
+
+#pragma unroll
+    for (int q = 0; q < 3; ++q) red[wave][q][lane] = acc[q];
+    __syncthreads();
+    if (wave != 0) return;
+    f32x4 P[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        P[q] = red[0][q][lane];
+#pragma unroll
+        for (int w = 1; w < WH_WAVES; ++w) P[q] += red[w][q][lane];
+    }
+    // lane (g, cb): rows 4 g + e, column 16 grp + cb
+    const int n = 16 * grp + cb;
+    const float cn = a.c[n];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int m = 4 * g + e;
+        if (m >= M) continue;
+        float y = cn;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            float mu = 0.f, r = 1.f;
+            if (NORM != NORM_NONE) {
+                const float stt[3] = {sst[q * M + m][0], sst[q * M + m][1], sst[q * M + m][2]};
+                row_norm<NORM>(stt, d, a.eps, mu, r);
+            }
+            float pv = P[q][e];
+            if (NORM == NORM_LN) pv -= mu * a.u[(size_t)q * d + n];
+            y += (NORM == NORM_NONE) ? pv : r * pv;
+        }
+        a.out[(size_t)m * d + n] = (uint16_t)(pack_bf2(y, 0.f) & 0xffffu);
+    }
+}
+
 // ----------------------------------------------------------------- host side
 GemvPlan plan_gemv(int M, int d, int norm) {
     (void)norm;
     GemvPlan p;
     p.MT = (M + 15) / 16;
     const int T3 = d / 32;
+    // a handful of tokens: the whole-K kernel when its token rows fit in LDS
+    // and its one-block-per-workgroup grid fills whole rounds of the CUs
+    if (M <= WH_MAXM && d % (32 * WH_WAVES) == 0 && M * (6 * d + 64) <= WH_A_BYTES &&
+        (d / 16 <= 256 || (d / 16) % 256 == 0)) {
+        const int JS = T3 / WH_WAVES;
+        int ring = 8;
+        while (ring > 1 && (JS % ring || JS < ring)) ring >>= 1;
+        if (JS % ring == 0 && JS >= ring) {
+            p.whole = 1;
+            p.ring = ring;
+            p.waves = WH_WAVES;
+            p.kps = 1;
+            p.nb = 1;
+            p.grid = d / 16;
+            p.counters_bytes = 256;
+            p.part_bytes = 256;
+            return p;
+        }
+    }
     // Column blocks per workgroup: 8 (128 columns) from two token tiles on,
     // which halves how often the workgroups re-read the hidden states; the
     // wider tile then keeps fewer k-steps in flight (registers).
@@ -591,7 +771,27 @@ static hipError_t launch_gn(const GemvArgs& a, const GemvPlan& p, hipStream_t st
     }
 }
 
+template <int NORM>
+static hipError_t launch_whole(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
+    switch (p.ring) {
+        case 8: gemv_whole_kernel<NORM, 8><<<p.grid, 64 * WH_WAVES, 0, st>>>(a); break;
+        case 4: gemv_whole_kernel<NORM, 4><<<p.grid, 64 * WH_WAVES, 0, st>>>(a); break;
+        case 2: gemv_whole_kernel<NORM, 2><<<p.grid, 64 * WH_WAVES, 0, st>>>(a); break;
+        case 1: gemv_whole_kernel<NORM, 1><<<p.grid, 64 * WH_WAVES, 0, st>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv(const GemvArgs& a, int norm, const GemvPlan& p, hipStream_t st) {
+    if (p.whole) {
+        if (a.M < 1 || a.M > WH_MAXM || a.M * (6 * a.d + 64) > WH_A_BYTES || a.d % (32 * WH_WAVES) ||
+            p.grid != a.d / 16)
+            return hipErrorInvalidValue;
+        if (norm == NORM_LN) return launch_whole<NORM_LN>(a, p, st);
+        if (norm == NORM_RMS) return launch_whole<NORM_RMS>(a, p, st);
+        return launch_whole<NORM_NONE>(a, p, st);
+    }
     if (p.waves < 1 || p.waves > GV_WAVES || a.waves != p.waves || a.M < 1 || a.M > DECODE_MAX_M ||
         64 * p.waves < 16 * p.nb || a.d % (16 * p.nb))
         return hipErrorInvalidValue;

@@ -74,6 +74,7 @@ struct GemvArgs {
 
 struct GemvPlan {
     int kps = 0, ring = 0, waves = 0, nb = 4, MT = 1, grid = 0;  // nb: 16-column blocks per workgroup
+    int whole = 0;  // 1: few tokens, the whole-K kernel (one 16-column block per workgroup, no split)
     size_t counters_bytes = 0, part_bytes = 0;
     static constexpr size_t rstats_bytes = 3 * 64 * 4 * sizeof(uint32_t);
 };
