@@ -177,8 +177,10 @@ int eagle31_release(void);
 
 /*
  * eagle31_debug_stats_recompute - test hook for the folded decode path
- * (eagle31_fuse_folded with M <= 64).  That kernel computes each token's
- * statistics once and hands them between workgroups through the workspace;
+ * (eagle31_fuse_folded with 2 <= M <= 64; a one-token call computes the
+ * statistics in every workgroup and hands nothing over, so the hook does not
+ * change it).  That kernel computes each token's statistics once and hands
+ * them between workgroups through the workspace;
  * a reader waits a bounded time for them and, if they are not there, computes
  * the rows itself with the same arithmetic.  With on != 0 every reader takes
  * that fallback at once, so a test can check that it gives the same bits.
