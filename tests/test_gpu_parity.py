@@ -352,6 +352,25 @@ def test_two_streams_use_their_own_workspaces():
     assert_parity(bf16_to_f64(refC), oracle_rows(inpC, LN, 1e-5), "two streams, prefill path")
 
 
+@pytest.mark.parametrize("d", [512, 1024, 2048, 3072, 4096])
+@pytest.mark.parametrize("kind", [LN, RMS, NONE])
+def test_one_token_kernel_widths(d, kind):
+    """A single token goes through the whole-K kernel (one 16-column block per
+    workgroup, statistics from each workgroup's LDS copy of the token): at
+    widths that change its ring depth and grid, for every norm."""
+    note(f"one token d={d} kind={kind}")
+    w = synth.gen.custom_workload(d, (1,), seed_tag=d + 7 * kind)
+    inp = synth.make_inputs(w, 1)
+    dv = DevInputs(inp)
+    eps = 1e-5 if kind == LN else (1e-6 if kind == RMS else 0.0)
+    wf, u, c = e31().fold_prepare(kind, dv.gamma, dv.beta, dv.W, dv.bias)
+    out = e31().fuse_folded(dv.h[0], dv.h[1], dv.h[2], kind, eps, wf, u, c)
+    again = e31().fuse_folded(dv.h[0], dv.h[1], dv.h[2], kind, eps, wf, u, c)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16))
+    assert_parity(bf16_to_f64(out), oracle_rows(inp, kind, eps), f"one token d={d} kind={kind}")
+
+
 def test_optional_parameters_absent():
     """gamma = None means 1, beta = None means 0, bias = None means none."""
     note("optional params")
