@@ -452,8 +452,207 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
     if (tid == 0) __hip_atomic_store(a.counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// =====================================================================
+// One token on the stored W: normalise first, then a VALU GEMV
+// =====================================================================
+//
+// With one token the normalised activation is a vector of 3d floats, so it
+// is computed exactly (fp32) before the contraction and no state boundary or
+// fold is involved: out = xn . W + bias, xn = [n(h_low) | n(h_mid) | n(h_high)].
+// Workgroup (group g, chunk c) owns columns [512 g, 512 g + 512) -- 1 KiB of
+// every row of W -- and K rows [c R, c R + R).  It computes the three rows'
+// statistics itself (shifted sums, one wave per row), writes its xn rows to
+// LDS, then wave w takes rows w, w + 8, ...: each load instruction is one
+// contiguous 1 KiB piece of a row (lane l: columns 8 l .. 8 l + 7), 8 fp32
+// FMAs per row and lane.  The waves' sums are added in wave order and the
+// chunks of a group in chunk order by the last to arrive (device-coherent
+// partials and counter, as in the other decode kernels): the result is
+// bitwise reproducible.
+constexpr int ONE_ROWS_MAX = 16384;  // K rows per chunk (64 KiB of fp32 in LDS)
+
+__device__ __forceinline__ void one_row_sums(const uint16_t* row, int d, int lane, bool shift, float& K, float& S1,
+                                             float& S2) {
+    K = 0.f;
+    if (shift) {
+        const uint4 x = *reinterpret_cast<const uint4*>(row + 8 * (lane & 3));
+        float v = ((bf_lo(x.x) + bf_hi(x.x)) + (bf_lo(x.y) + bf_hi(x.y))) +
+                  ((bf_lo(x.z) + bf_hi(x.z)) + (bf_lo(x.w) + bf_hi(x.w)));
+        v += __shfl_xor(v, 1, 64);
+        v += __shfl_xor(v, 2, 64);
+        K = v * (1.0f / 32.0f);
+    }
+    // chunks lane, lane + 64, ... in order; the 8 loads of a batch are
+    // issued before any is used (one round trip per 4096 values)
+    float s1 = 0.f, s2 = 0.f;
+    const int nchunk = d >> 3;
+    for (int c0 = 0; c0 < nchunk; c0 += 512) {
+        uint4 x[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int c = c0 + lane + 64 * q;
+            x[q] = c < nchunk ? *reinterpret_cast<const uint4*>(row + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            if (c0 + lane + 64 * q >= nchunk) continue;
+            const uint32_t w4[4] = {x[q].x, x[q].y, x[q].z, x[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x0 = bf_lo(w4[e]) - K, x1 = bf_hi(w4[e]) - K;
+                s1 += x0 + x1;
+                s2 = fmaf(x0, x0, fmaf(x1, x1, s2));
+            }
+        }
+    }
+    S1 = wave_sum(s1);
+    S2 = wave_sum(s2);
+}
+
+template <int NORM>
+__global__ __launch_bounds__(512) void decode_one_kernel(DecodeArgs a) {
+    constexpr int R = 8;  // load ring (one 8-row x 128-byte load per step)
+    __shared__ float xn[ONE_ROWS_MAX];
+    __shared__ float st[3][2];       // mu, rstd per state
+    __shared__ float red[8][512];
+    __shared__ int sh_last;
+    const int d = a.d, ngroups = a.nb, nkc = a.kps;
+    const int rows = 3 * d / nkc;    // a multiple of 64 (8 waves x an 8-row ring)
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int per = (ngroups * nkc + 7) >> 3;
+    const int lin = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    if (lin >= ngroups * nkc) return;
+    const int grp = lin / nkc, kc = lin - grp * nkc;
+    const int n0 = 512 * grp, k0 = kc * rows;
+
+    // this wave's W rows: k0 + wave + 8 i, columns n0 + 8 lane .. + 7
+    const uint16_t* __restrict__ wp = a.W + (size_t)(k0 + wave) * d + n0 + 8 * lane;
+    const size_t wstep = (size_t)8 * d;
+    const int nsteps = rows / 8;     // a multiple of R
+    uint4 rw[R];
+#pragma unroll
+    for (int p = 0; p < R; ++p) rw[p] = *reinterpret_cast<const uint4*>(wp + (size_t)p * wstep);
+
+    // statistics of the three rows (waves 0..2)
+    if (NORM != NORM_NONE && wave < 3) {
+        float K, S1, S2;
+        one_row_sums(a.h[wave], d, lane, NORM == NORM_LN, K, S1, S2);
+        if (lane == 0) {
+            const float inv_d = 1.0f / (float)d;
+            float mu = 0.f, rstd;
+            if (NORM == NORM_LN) {
+                const float dm = S1 * inv_d;
+                mu = K + dm;
+                rstd = 1.0f / sqrtf(fmaxf(S2 * inv_d - dm * dm, 0.f) + a.eps);
+            } else {
+                rstd = 1.0f / sqrtf(S2 * inv_d + a.eps);
+            }
+            st[wave][0] = mu;
+            st[wave][1] = rstd;
+        }
+    }
+    __syncthreads();
+    // xn of this chunk's rows, in fp32
+    for (int r = tid; r < rows; r += 512) {
+        const int k = k0 + r, s = k / d, kk = k - s * d;
+        const uint16_t* hs = s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2]);
+        float x = bf_one(hs[kk]);
+        if (NORM != NORM_NONE) {
+            const uint16_t* gs = s == 0 ? a.gamma[0] : (s == 1 ? a.gamma[1] : a.gamma[2]);
+            const float gm = gs ? bf_one(gs[kk]) : 1.f;
+            x = (x - st[s][0]) * st[s][1] * gm;
+            if (NORM == NORM_LN) {
+                const uint16_t* bs = s == 0 ? a.beta[0] : (s == 1 ? a.beta[1] : a.beta[2]);
+                if (bs) x += bf_one(bs[kk]);
+            }
+        }
+        xn[r] = x;
+    }
+    __syncthreads();
+
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    const float* xr = xn + wave;
+    auto fma_row = [&](const uint4& w, float x) __attribute__((always_inline)) {
+        const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = fmaf(x, bf_lo(w4[e]), acc[2 * e]);
+            acc[2 * e + 1] = fmaf(x, bf_hi(w4[e]), acc[2 * e + 1]);
+        }
+    };
+    int i = 0;
+    for (; i < nsteps - R; i += R) {
+#pragma unroll
+        for (int p = 0; p < R; ++p) {
+            fma_row(rw[p], xr[(i + p) * 8]);
+            rw[p] = *reinterpret_cast<const uint4*>(wp + (size_t)(i + p + R) * wstep);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < R; ++p) fma_row(rw[p], xr[(i + p) * 8]);
+
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wave][8 * lane + e] = acc[e];
+    __syncthreads();
+    // thread t < 512: column n0 + t, the waves' sums in wave order
+    float* part = a.part + ((size_t)grp * nkc + kc) * 512;
+    {
+        float v = red[0][tid];
+#pragma unroll
+        for (int w = 1; w < 8; ++w) v += red[w][tid];
+        store_coherent(part + tid, v);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(a.counters + grp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sh_last = (old == nkc - 1);
+    }
+    __syncthreads();
+    if (!sh_last) return;
+    {
+        // chunks summed in order; each batch of 8 loads is issued before use
+        const float* gp = a.part + (size_t)grp * nkc * 512 + tid;
+        float y = 0.f;
+        for (int c0 = 0; c0 < nkc; c0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = c0 + q < nkc ? load_coherent(gp + (size_t)(c0 + q) * 512) : 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (c0 + q < nkc) y += v[q];
+        }
+        if (a.bias) y += bf_one(a.bias[n0 + tid]);
+        a.out[n0 + tid] = (uint16_t)(pack_bf2(y, 0.f) & 0xffffu);
+    }
+    if (tid == 0) __hip_atomic_store(a.counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 DecodePlan plan_decode(int M, int d, int norm) {
     DecodePlan p;
+    // one token: the VALU kernel, 512-column groups x K chunks, the most
+    // workgroups up to one per CU, each wave a multiple of 8 load steps
+    if (M == 1 && d % 512 == 0) {
+        const int ngroups = d / 512;
+        int best = 0;
+        for (int nkc = 1; nkc <= 256 && ngroups * nkc <= 256; ++nkc) {
+            if ((3 * d) % (nkc * 64) != 0) continue;  // rows per chunk: 8 waves x a multiple of 8 steps
+            if (3 * d / nkc > ONE_ROWS_MAX) continue;
+            best = nkc;
+        }
+        if (best) {
+            p.one = 1;
+            p.nb = ngroups;
+            p.kps = best;
+            p.counters_bytes = ((size_t)ngroups * sizeof(int) + 255) / 256 * 256;
+            p.stats_bytes = 256;
+            p.part_bytes = ((size_t)ngroups * best * 512 * sizeof(float) + 255) / 256 * 256;
+            return p;
+        }
+    }
     const int rows = M + (norm == NORM_LN ? 2 : 0);
     p.MT = (rows + 15) / 16;
     p.J = p.MT <= 2 ? 8 : 4;
@@ -492,7 +691,22 @@ static hipError_t launch_decode_n(const DecodeArgs& a, const DecodePlan& p, hipS
     }
 }
 
+template <int NORM>
+static hipError_t launch_one(const DecodeArgs& a, const DecodePlan& p, hipStream_t st) {
+    const int grid = ((p.nb * p.kps + 7) / 8) * 8;
+    decode_one_kernel<NORM><<<grid, 512, 0, st>>>(a);
+    return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a, int norm, const DecodePlan& p, hipStream_t st) {
+    if (p.one) {
+        if (a.M != 1 || a.nb != p.nb || a.kps != p.kps || a.d != 512 * p.nb || (3 * a.d) % (p.kps * 64) ||
+            3 * a.d / p.kps > ONE_ROWS_MAX)
+            return hipErrorInvalidValue;
+        if (norm == NORM_LN) return launch_one<NORM_LN>(a, p, st);
+        if (norm == NORM_RMS) return launch_one<NORM_RMS>(a, p, st);
+        return launch_one<NORM_NONE>(a, p, st);
+    }
     if (norm == NORM_LN) return launch_decode_n<NORM_LN>(a, p, st);
     if (norm == NORM_RMS) return launch_decode_n<NORM_RMS>(a, p, st);
     return launch_decode_n<NORM_NONE>(a, p, st);

@@ -32,6 +32,7 @@ struct DecodeArgs {
 
 struct DecodePlan {
     int J = 8, MT = 1, nb = 0, kps = 0;
+    int one = 0;  // 1: one token, the VALU kernel (nb groups of 64 columns x kps K chunks)
     size_t counters_bytes = 0, stats_bytes = 0, part_bytes = 0;
     size_t total() const { return counters_bytes + stats_bytes + part_bytes; }
 };

@@ -352,7 +352,7 @@ def test_two_streams_use_their_own_workspaces():
     assert_parity(bf16_to_f64(refC), oracle_rows(inpC, LN, 1e-5), "two streams, prefill path")
 
 
-@pytest.mark.parametrize("d", [512, 1024, 2048, 3072, 4096])
+@pytest.mark.parametrize("d", [512, 1024, 2048, 3072, 4096, 5120, 8192])
 @pytest.mark.parametrize("kind", [LN, RMS, NONE])
 def test_one_token_kernel_widths(d, kind):
     """A single token goes through the whole-K kernel (one 16-column block per
@@ -369,6 +369,16 @@ def test_one_token_kernel_widths(d, kind):
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), again.view(torch.int16))
     assert_parity(bf16_to_f64(out), oracle_rows(inp, kind, eps), f"one token d={d} kind={kind}")
+    # the stored-weight entry point (its own one-token kernel), with and
+    # without the optional parameters
+    Y = oracle_rows(inp, kind, eps)
+    G = run_fuse(dv, kind, eps)
+    assert_parity(G, Y, f"one token stored W d={d} kind={kind}")
+    assert np.array_equal(G, run_fuse(dv, kind, eps))
+    if kind != NONE:
+        G0 = run_fuse(dv, kind, eps, use_gamma=False, use_beta=False, use_bias=False)
+        Y0 = oracle_rows(inp, kind, eps, use_gamma=False, use_beta=False, use_bias=False)
+        assert_parity(G0, Y0, f"one token stored W, no parameters, d={d} kind={kind}")
 
 
 def test_optional_parameters_absent():
