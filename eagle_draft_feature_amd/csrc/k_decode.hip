@@ -370,19 +370,34 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
     // statistics of every state and token (float64 combination of the pieces)
     float* sh_delta = sh_big;  // [3 * PPS][64]: mu_s - K_p
     for (int m = tid; m < M; m += DTHREADS) {
+        // every state's piece records are loaded before any is used (one
+        // round trip, not one per state)
+        // (unconditional loads: a piece that does not exist reads slot 0,
+        // inside the workspace, and its values are dropped; a load under a
+        // branch would get a wait of its own)
+        float Ka[3][PPS], s1a[3][PPS], s2a[3][PPS];
 #pragma unroll
-        for (int ss = 0; ss < 3; ++ss) {
-            float K[PPS], s1[PPS], s2[PPS];
+        for (int ss = 0; ss < 3; ++ss)
 #pragma unroll
             for (int q = 0; q < PPS; ++q) {
-                K[q] = s1[q] = s2[q] = 0.f;
-                if (NORM != NORM_NONE && pval[ss][q]) {
+                Ka[ss][q] = s1a[ss][q] = s2a[ss][q] = 0.f;
+                if (NORM != NORM_NONE) {
                     const float* st = a.stats + ((size_t)pslot[ss][q] * DECODE_MAX_M + m) * 3;
-                    K[q] = load_coherent(st);
-                    s1[q] = load_coherent(st + 1);
-                    s2[q] = load_coherent(st + 2);
+                    Ka[ss][q] = load_coherent(st);
+                    s1a[ss][q] = load_coherent(st + 1);
+                    s2a[ss][q] = load_coherent(st + 2);
                 }
             }
+#pragma unroll
+        for (int ss = 0; ss < 3; ++ss)
+#pragma unroll
+            for (int q = 0; q < PPS; ++q)
+                if (!pval[ss][q]) Ka[ss][q] = s1a[ss][q] = s2a[ss][q] = 0.f;
+#pragma unroll
+        for (int ss = 0; ss < 3; ++ss) {
+            const float* K = Ka[ss];
+            const float* s1 = s1a[ss];
+            const float* s2 = s2a[ss];
             double r = 1.0, mu = 0.0;
             if (NORM == NORM_LN) {
                 double sum = 0.0;
@@ -418,16 +433,21 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
     for (int ss = 0; ss < 3; ++ss)
 #pragma unroll
         for (int q = 0; q < PPS; ++q) {
+            // unconditional loads (rows clamped, missing pieces read slot 0),
+            // the values of rows and pieces that do not exist are dropped
             const float* base = a.part + (size_t)pslot[ss][q] * TILE;
             U[ss][q] = 0.f;
-            if (NORM == NORM_LN && pval[ss][q]) {
-                U[ss][q] = load_coherent(base + M * NW + n);
-                add += load_coherent(base + (M + 1) * NW + n);
+            if (NORM == NORM_LN) {
+                const float uv = load_coherent(base + M * NW + n);
+                const float av = load_coherent(base + (M + 1) * NW + n);
+                U[ss][q] = pval[ss][q] ? uv : 0.f;
+                add += pval[ss][q] ? av : 0.f;
             }
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const int m = rg + RG * i;
-                P[ss][q][i] = (pval[ss][q] && m < M) ? load_coherent(base + m * NW + n) : 0.f;
+                const float pv = load_coherent(base + min(m, M - 1) * NW + n);
+                P[ss][q][i] = (pval[ss][q] && m < M) ? pv : 0.f;
             }
         }
     if (a.bias != nullptr) add += bf_one(a.bias[n0 + n]);
