@@ -186,13 +186,12 @@ __device__ void stats_gather(const GemvArgs& a, int lane, float (*out)[3]) {
     const int need = 3 * a.M;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     bool ready = false;
+    // (every load below is unconditional, its row clamped to the last one:
+    // loads under a branch would each get a wait of their own)
     for (; !a.stats_recompute;) {
         uint32_t f[MAXR / 64];
 #pragma unroll
-        for (int j = 0; j < MAXR / 64; ++j) {
-            const int it = lane + 64 * j;
-            f[j] = it < need ? load_coherent_u32(a.rstats + 4 * it + 3) : a.call_id;
-        }
+        for (int j = 0; j < MAXR / 64; ++j) f[j] = load_coherent_u32(a.rstats + 4 * min(lane + 64 * j, need - 1) + 3);
         bool mine = true;
 #pragma unroll
         for (int j = 0; j < MAXR / 64; ++j) mine &= f[j] == a.call_id;
@@ -207,8 +206,8 @@ __device__ void stats_gather(const GemvArgs& a, int lane, float (*out)[3]) {
         float v[3 * MAXR / 64];
 #pragma unroll
         for (int j = 0; j < 3 * MAXR / 64; ++j) {
-            const int i = lane + 64 * j, it = i / 3;
-            v[j] = i < 3 * need ? __uint_as_float(load_coherent_u32(a.rstats + 4 * it + (i - 3 * it))) : 0.f;
+            const int i = min(lane + 64 * j, 3 * need - 1), it = i / 3;
+            v[j] = __uint_as_float(load_coherent_u32(a.rstats + 4 * it + (i - 3 * it)));
         }
 #pragma unroll
         for (int j = 0; j < 3 * MAXR / 64; ++j) {
