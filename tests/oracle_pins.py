@@ -320,3 +320,56 @@ def check_fold_identity(fuse_fn, fold_prepare, fold_apply, seed=13, d=32, M=9) -
         if np.max(np.abs(Yf - Y)) > 1e-12 * max(1.0, np.max(np.abs(Y))):
             return False
     return True
+
+
+# ---------------------------------------------------------------------------
+# Post-norm hidden-state feedback: norm_fn(X, kind, eps, gamma, beta) -> [M, d]
+# ---------------------------------------------------------------------------
+
+
+def check_norm_output_torch(norm_fn, seed=17, d=96, M=7, tol=1e-12) -> bool:
+    """Against torch's CPU float64 layer_norm / rms_norm (an independent
+    library implementation), with and without gamma / beta; NONE returns x."""
+    import torch
+    import torch.nn.functional as F
+
+    rng = np.random.default_rng(seed)
+    X = rng.normal(0, 6.0, (M, d)) + rng.normal(0, 2.0, d)
+    g = rng.normal(1, 0.2, d)
+    b = rng.normal(0, 0.1, d)
+    t = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a))
+    for gg, bb in ((g, b), (None, None), (g, None), (None, b)):
+        ref = F.layer_norm(t(X), (d,), t(gg), t(bb), 1e-5).numpy()
+        if np.max(np.abs(norm_fn(X, NORM_LN, 1e-5, gg, bb) - ref)) > tol * max(1.0, np.max(np.abs(ref))):
+            return False
+        ref = F.rms_norm(t(X), (d,), t(gg), 1e-6).numpy()
+        # beta is not part of an RMSNorm: passing one must change nothing
+        if np.max(np.abs(norm_fn(X, NORM_RMS, 1e-6, gg, bb) - ref)) > tol * max(1.0, np.max(np.abs(ref))):
+            return False
+    return bool(np.array_equal(norm_fn(X, NORM_NONE, 1e-5, g, b), X))
+
+
+def check_norm_output_closed_forms(norm_fn, tol=1e-13) -> bool:
+    """Rows whose statistics are known by hand.
+
+    [1, 2, 3, 4]: mean 2.5, biased variance 1.25, mean square 7.5.
+    A constant row c: LayerNorm gives beta exactly; RMSNorm c / sqrt(c^2 + eps).
+    An alternating row +a, -a: mean 0, variance and mean square a^2.
+    """
+    g = np.array([1.0, 2.0, -0.5, 4.0])
+    b = np.array([0.25, -1.0, 0.0, 3.0])
+    x = np.array([[1.0, 2.0, 3.0, 4.0]])
+    ok = np.allclose(norm_fn(x, NORM_LN, 0.0, None, None)[0], np.array([-1.5, -0.5, 0.5, 1.5]) / np.sqrt(1.25),
+                     rtol=0, atol=tol)
+    ok &= np.allclose(norm_fn(x, NORM_LN, 0.75, g, b)[0], np.array([-1.5, -0.5, 0.5, 1.5]) / np.sqrt(2.0) * g + b,
+                      rtol=0, atol=tol)
+    ok &= np.allclose(norm_fn(x, NORM_RMS, 0.5, g, None)[0], x[0] / np.sqrt(8.0) * g, rtol=0, atol=tol)
+    c = np.full((2, 4), 3.0)
+    c[1] = -0.125
+    ok &= np.array_equal(norm_fn(c, NORM_LN, 1e-5, g, b), np.stack([b, b]))
+    ok &= np.allclose(norm_fn(c, NORM_RMS, 1e-2, g, None), c / np.sqrt(c * c + 1e-2) * g, rtol=0, atol=tol)
+    a = np.array([[5.0, -5.0, 5.0, -5.0]])
+    want = a / np.sqrt(25.0 + 1e-3) * g
+    ok &= np.allclose(norm_fn(a, NORM_LN, 1e-3, g, b), want + b, rtol=0, atol=tol)
+    ok &= np.allclose(norm_fn(a, NORM_RMS, 1e-3, g, b), want, rtol=0, atol=tol)
+    return bool(ok)

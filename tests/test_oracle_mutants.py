@@ -109,3 +109,38 @@ def test_reference_copy_of_oracle_passes():
 def test_mutant_is_caught(name):
     res = _all_pins(MUTANTS[name])
     assert not all(res.values()), f"mutant {name} passed every pin: {res}"
+
+
+# --- post-norm feedback: planted slips in the row norm -----------------------
+
+
+def _postnorm_mutant(slip):
+    def norm_fn(X, kind, eps, g, b):
+        X = np.asarray(X, float)
+        d = X.shape[1]
+        g = np.ones(d) if g is None else np.asarray(g, float)
+        b = np.zeros(d) if b is None else np.asarray(b, float)
+        if kind == NONE:
+            return X.copy()
+        if kind == LN:
+            mu = X.mean(axis=1, keepdims=True)
+            var = ((X - mu) ** 2).sum(axis=1, keepdims=True) / (d - 1 if slip == "unbiased" else d)
+            r = 1.0 / (np.sqrt(var) + eps) if slip == "eps_outside" else 1.0 / np.sqrt(var + eps)
+            return (X - mu) * r * g + (0.0 if slip == "no_beta" else b)
+        mu = X.mean(axis=1, keepdims=True) if slip == "rms_centres" else 0.0
+        r = 1.0 / np.sqrt(((X - mu) ** 2).mean(axis=1, keepdims=True) + eps)
+        out = (X - mu) * r
+        return out if slip == "no_gamma" else out * g
+    return norm_fn
+
+
+@pytest.mark.parametrize("slip", ["unbiased", "eps_outside", "no_beta", "rms_centres", "no_gamma"])
+def test_postnorm_mutants_fail_a_pin(slip):
+    fn = _postnorm_mutant(slip)
+    assert not (pins.check_norm_output_torch(fn) and pins.check_norm_output_closed_forms(fn))
+
+
+def test_postnorm_mutant_harness_is_faithful():
+    """The unmutated copy passes every pin (so a failure above is the slip's)."""
+    fn = _postnorm_mutant(None)
+    assert pins.check_norm_output_torch(fn) and pins.check_norm_output_closed_forms(fn)

@@ -130,3 +130,21 @@ def test_generator_distribution_recipe():
     colstd = np.std(H[2], axis=0)
     top = np.sort(colstd)[-8:]
     assert np.all(top > 10 * np.median(colstd))
+
+
+def test_norm_output_torch_library_cross_check():
+    assert pins.check_norm_output_torch(oracle.norm_output)
+
+
+def test_norm_output_closed_forms():
+    assert pins.check_norm_output_closed_forms(oracle.norm_output)
+
+
+def test_norm_output_bits_decodes_like_fuse_inputs():
+    """norm_output_bits on generated bf16 rows equals norm_output on the
+    exactly decoded values (row 0 of the low state and its parameters)."""
+    inp = synth.make_inputs(1, M=8, with_weights=False)
+    got = oracle.norm_output_bits(inp.h[0], oracle.NORM_LN, 1e-5, inp.gamma[0], inp.beta[0])
+    want = oracle.norm_output(oracle.decode_bf16(inp.h[0]), oracle.NORM_LN, 1e-5, oracle.decode_bf16(inp.gamma[0]),
+                              oracle.decode_bf16(inp.beta[0]))
+    assert np.array_equal(got, want)
