@@ -50,7 +50,7 @@ def parse():
     p.add_argument("--no-sweep", action="store_true", help="skip the per-M decode sweep")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurements")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
-    p.add_argument("--only", choices=["decode", "decode_folded", "prefill", "rowstats", "copy"], default=None,
+    p.add_argument("--only", choices=["decode", "decode_folded", "prefill", "rowstats", "copy", "postnorm"], default=None,
                    help="run a single leg (used under rocprofv3)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
@@ -250,6 +250,33 @@ def prefill_leg(torch, pkg, synth, cfg, M, kind, eps, steps, warmup, folded=Fals
     return res
 
 
+def postnorm_leg(torch, pkg, synth, cfg, M, kind, eps, steps, warmup):
+    """eagle31_norm_output (post-norm feedback) on one workload's hidden-state
+    shape: x read once, out written once, gamma and beta read once per call;
+    cold-cache rotation over distinct copies of x and out."""
+    inp = synth.make_inputs(cfg, M, with_weights=False)
+    d = inp.d
+    R = 2 if 2 * M * d * 2 >= MALL_BYTES else rotation_count(2 * M * d * 2)
+    x0 = to_dev(inp.h[2])
+    xs = [x0] + [x0.clone() for _ in range(R - 1)]
+    outs = [torch.empty_like(x0) for _ in range(R)]
+    g, b = to_dev(inp.gamma[2]), to_dev(inp.beta[2])
+    name = synth.workloads.NORM_NAMES[kind]
+
+    def fn(i):
+        pkg.norm_output(xs[i], name, eps, g, b if kind == 1 else None, out=outs[i])
+
+    t, _ = time_loop(torch, fn, R, steps, warmup)
+    per = t / steps
+    nbytes = 2 * M * d * 2 + (2 if kind == 1 else 1) * d * 2
+    res = dict(entry="eagle31_norm_output", kernel="norm_rows_kernel", workload=synth.CONFIGS[cfg].name, d=d, M=M,
+               norm=name, steps=steps, R=R, us_per_call=round(per * 1e6, 3), bytes_per_call=nbytes,
+               gbs=round(nbytes / per / 1e9, 1), hbm_frac=round(nbytes / per / 1e9 / HBM_PEAK_GBS, 4))
+    del xs, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline_leg(inp, kind, eps, budget_s):
     """The fp64 oracle as it stands, on preconverted float64 arrays, repeated
     until about budget_s seconds of host work."""
@@ -317,6 +344,9 @@ def main():
     if args.only == "prefill":
         print(json.dumps(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, max(3, args.steps), args.warmup, folded=True)))
         return
+    if args.only == "postnorm":
+        print(json.dumps(postnorm_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, max(5, args.steps), args.warmup)))
+        return
     if args.only == "rowstats":
         inp = synth.make_inputs(4, with_weights=False)
         h = [to_dev(x) for x in inp.h]
@@ -379,6 +409,12 @@ def main():
                 others.append(prefill_leg(torch, pkg, synth, 5, M, kind, eps, 30 if M < 4000 else 20, 5,
                                           folded=True))
 
+    # the post-norm feedback of the drafter output (a next step of the path),
+    # at the decode batch's and the prefill batch's shapes
+    postnorm = [postnorm_leg(torch, pkg, synth, 2, 64, 1, 1e-5, 400, 50)]
+    if not args.no_prefill:
+        postnorm.append(postnorm_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, 20, 5))
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline_leg(dec["inp"], dec["kind"], dec["eps"], args.cpu_seconds)
@@ -406,6 +442,7 @@ def main():
         "decode_sweep": sweep,
         "prefill": prefill,
         "other_workloads": others,
+        "postnorm": postnorm,
     }
     print(json.dumps(line))
 

@@ -451,6 +451,30 @@ int eagle31_row_stats(const void* h_low, const void* h_mid, const void* h_high, 
     return EAGLE31_OK;
 }
 
+int eagle31_norm_output(const void* x, int64_t M, int64_t d, int norm_kind, float eps, const void* gamma,
+                        const void* beta, void* out, void* stream) {
+    int r = check_common(M, d, norm_kind, eps);
+    if (r != EAGLE31_OK) return r;
+    if (d > NORM_ROWS_MAX_D) return EAGLE31_ERR_SHAPE;
+    if (M == 0) return EAGLE31_OK;
+    if (x == nullptr || out == nullptr) return EAGLE31_ERR_NULL;
+    const bool use_g = norm_kind != EAGLE31_NORM_NONE && gamma != nullptr;
+    const bool use_b = norm_kind == EAGLE31_NORM_LAYERNORM && beta != nullptr;
+    if (!aligned16(x) || !aligned16(out) || (use_g && !aligned16(gamma)) || (use_b && !aligned16(beta)))
+        return EAGLE31_ERR_ALIGN;
+    // out == x is the in-place form; any other overlap is refused
+    const size_t rb = (size_t)M * (size_t)d * 2;
+    if ((out != x && overlaps(out, rb, x, rb)) || (use_g && overlaps(out, rb, gamma, (size_t)d * 2)) ||
+        (use_b && overlaps(out, rb, beta, (size_t)d * 2)))
+        return EAGLE31_ERR_ALIAS;
+    const hipError_t e = launch_norm_rows(static_cast<const uint16_t*>(x), (int)M, (int)d, norm_kind, eps,
+                                          use_g ? static_cast<const uint16_t*>(gamma) : nullptr,
+                                          use_b ? static_cast<const uint16_t*>(beta) : nullptr,
+                                          static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return EAGLE31_OK;
+}
+
 const char* eagle31_status_string(int status) {
     switch (status) {
         case EAGLE31_OK: return "ok";

@@ -8,6 +8,11 @@
 namespace e31 {
 
 // ---------------------------------------------------------------- row stats
+// Post-norm feedback rows (out = norm(x) * gamma + beta, one row per wave).
+constexpr int NORM_ROWS_MAX_D = 8192;
+hipError_t launch_norm_rows(const uint16_t* x, int M, int d, int norm, float eps, const uint16_t* gamma,
+                            const uint16_t* beta, uint16_t* out, hipStream_t st);
+
 hipError_t launch_row_stats(const uint16_t* h0, const uint16_t* h1, const uint16_t* h2, int M, int d, int norm,
                             float eps, float* mu, float* rstd, hipStream_t st);
 

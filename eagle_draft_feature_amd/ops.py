@@ -177,6 +177,26 @@ def row_stats(h_low, h_mid, h_high, norm, eps):
     return mu, rstd
 
 
+def norm_output(x, norm, eps, gamma=None, beta=None, out=None):
+    """eagle31_norm_output: row norm of the drafter's output hidden state x
+    [M, d] bf16 (post-norm feedback).  out=x normalises in place."""
+    _want(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [M, d]")
+    M, d = x.shape
+    if gamma is not None:
+        _want(gamma, "gamma", shape=(d,), device=x.device)
+    if beta is not None:
+        _want(beta, "beta", shape=(d,), device=x.device)
+    if out is None:
+        out = torch.empty((M, d), dtype=torch.bfloat16, device=x.device)
+    _want(out, "out", shape=(M, d), device=x.device)
+    st = lib().eagle31_norm_output(_ptr(x), M, d, norm_kind(norm), float(eps), _ptr(gamma), _ptr(beta), _ptr(out),
+                                   _stream(x))
+    check("eagle31_norm_output", st)
+    return out
+
+
 def release() -> None:
     check("eagle31_release", lib().eagle31_release())
 

@@ -165,6 +165,28 @@ int eagle31_fuse_folded_ws(const void* h_low, const void* h_mid, const void* h_h
 int eagle31_row_stats(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d,
                       int norm_kind, float eps, float* mu, float* rstd, void* stream);
 
+/*
+ * eagle31_norm_output - post-norm hidden-state feedback: the drafter's output
+ * hidden state x [M, d] is normalised row by row before it is fed to the next
+ * draft step (vLLM EAGLE 3.1 release post, devlery.com/blog/vllm-eagle31-attention-drift,
+ * sections "EAGLE 3.1이 바꾼 것은 작지만 낮은 계층입니다" and "vLLM main에 들어갔다는
+ * 것이 뉴스입니다"; the model card cited there names the layer norm_output):
+ *
+ *     out[m, :] = norm(x[m, :]) with the same three kinds as above, one gamma
+ *                 and one beta for every row.
+ *
+ * x, out: bf16 [M, d] row-major.  out == x (in place) is allowed; any other
+ *         overlap returns EAGLE31_ERR_ALIAS.
+ * gamma:  bf16 [d] or NULL (ones); ignored for EAGLE31_NORM_NONE.
+ * beta:   bf16 [d] or NULL (zeros); used by EAGLE31_NORM_LAYERNORM only.
+ * Statistics and arithmetic in float32, out rounded to nearest even;
+ * EAGLE31_NORM_NONE copies x.  d is limited to 8192 here (EAGLE31_ERR_SHAPE
+ * above); every other limit and convention is the shared one.  Needs no
+ * scratch memory.
+ */
+int eagle31_norm_output(const void* x, int64_t M, int64_t d, int norm_kind, float eps, const void* gamma,
+                        const void* beta, void* out, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* eagle31_status_string(int status);
 

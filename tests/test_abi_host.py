@@ -148,3 +148,35 @@ def test_stats_recompute_hook_is_host_only():
     assert L.eagle31_debug_stats_recompute(0) == 0
     e31.debug_stats_recompute(True)
     e31.debug_stats_recompute(False)
+
+
+def _norm_out(x=H0, M=64, d=4096, norm=1, eps=1e-5, g=WP, b=BP, out=OUT):
+    return e31.lib().eagle31_norm_output(x, M, d, norm, eps, g, b, out, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=8192 + 64), _capi.ERR_SHAPE),  # the post-norm kernel's row limit
+    (dict(d=96), _capi.ERR_SHAPE),
+    (dict(M=-1), _capi.ERR_SHAPE),
+    (dict(norm=7), _capi.ERR_NORM_KIND),
+    (dict(eps=float("nan")), _capi.ERR_EPS),
+    (dict(x=None), _capi.ERR_NULL),
+    (dict(out=None), _capi.ERR_NULL),
+    (dict(x=H0 + 2), _capi.ERR_ALIGN),
+    (dict(out=OUT + 8), _capi.ERR_ALIGN),
+    (dict(g=WP + 4), _capi.ERR_ALIGN),
+    (dict(b=BP + 2), _capi.ERR_ALIGN),
+    (dict(out=H0 + 16), _capi.ERR_ALIAS),  # partial overlap with x
+    (dict(out=WP - 64 * 4096 * 2 + 16), _capi.ERR_ALIAS),  # out's last row runs into gamma
+    (dict(out=BP - 1024), _capi.ERR_ALIAS),
+])
+def test_norm_output_rejects_bad_arguments(kw, code):
+    assert _norm_out(**kw) == code
+
+
+def test_norm_output_host_rules_for_parameters():
+    """M == 0 launches nothing; beta's alignment and overlap are not checked
+    where beta is unused (RMSNorm), nor gamma's for NONE."""
+    assert _norm_out(M=0) == _capi.OK
+    assert _norm_out(M=0, x=None, out=None) == _capi.OK
+    assert _norm_out(M=0, norm=2, b=BP + 2, d=8192 + 64) == _capi.ERR_SHAPE
