@@ -15,8 +15,12 @@
 // guarded load would get a wait of its own).  Such a lane also normalises and
 // stores that last piece, writing the very bytes its owner writes, so the
 // store side has no branch either.  gamma and beta are staged once per
-// workgroup into LDS as float32 and read from there for every row; a missing
-// gamma or beta arrives as a readable stand-in pointer with its flag off.
+// workgroup into LDS (bfloat16, 4*d bytes) and read from there for every row;
+// a missing gamma or beta arrives as a readable stand-in pointer with its flag
+// off.  Eight waves per workgroup and at most 128 registers per lane let four
+// waves share a SIMD, so 16 rows per CU are in flight: a wave's row is one
+// chain (load, reduce, store; the next row's loads wait for the stores'
+// completion as well), and the overlap between waves is what keeps HBM busy.
 #include <algorithm>
 
 #include "common.hpp"
@@ -24,39 +28,46 @@
 
 namespace e31 {
 
+constexpr int NR_WAVES = 8;
+
 template <int NORM, int P>
-__global__ __launch_bounds__(256) void norm_rows_kernel(const uint16_t* x, int M, int d, float eps,
+__global__ __launch_bounds__(64 * NR_WAVES) __attribute__((amdgpu_waves_per_eu(4))) void norm_rows_kernel(const uint16_t* x, int M, int d, float eps,
                                                         const uint16_t* __restrict__ gamma, int has_gamma,
                                                         const uint16_t* __restrict__ beta, int has_beta,
                                                         uint16_t* out) {
-    extern __shared__ float gb[];  // [d] gamma then [d] beta, float32
+    extern __shared__ u32x4 gb[];  // [d/8] gamma pieces then [d/8] beta pieces, bfloat16
     const int lane = threadIdx.x & 63;
     const int nvec = d >> 3;
     if (NORM != NORM_NONE) {
-        const uint4 ones = make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
-        for (int i = threadIdx.x; i < nvec; i += 256) {
-            const uint4 gl = reinterpret_cast<const uint4*>(gamma)[i];
-            const uint4 bl = reinterpret_cast<const uint4*>(beta)[i];
-            const uint4 g = has_gamma ? gl : ones;
-            const uint4 b = (NORM == NORM_LN && has_beta) ? bl : make_uint4(0u, 0u, 0u, 0u);
-            const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                gb[8 * i + 2 * q] = bf_lo(gw[q]);
-                gb[8 * i + 2 * q + 1] = bf_hi(gw[q]);
-                gb[d + 8 * i + 2 * q] = bf_lo(bw[q]);
-                gb[d + 8 * i + 2 * q + 1] = bf_hi(bw[q]);
-            }
+        const u32x4 ones = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}, zeros = {0u, 0u, 0u, 0u};
+        for (int i = threadIdx.x; i < nvec; i += 64 * NR_WAVES) {
+            const u32x4 gl = reinterpret_cast<const u32x4*>(gamma)[i];
+            const u32x4 bl = reinterpret_cast<const u32x4*>(beta)[i];
+            gb[i] = has_gamma ? gl : ones;
+            gb[nvec + i] = (NORM == NORM_LN && has_beta) ? bl : zeros;
         }
         __syncthreads();
     }
     const float inv_d = 1.0f / (float)d;
-    const int nwaves = gridDim.x * 4;
-    for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < M; row += nwaves) {
-        const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)row * d);
-        uint4 v[P];
+    const int nwaves = gridDim.x * NR_WAVES;
+    for (int row = blockIdx.x * NR_WAVES + (threadIdx.x >> 6); row < M; row += nwaves) {
+        // buffer accesses over the row: one 32-bit offset per piece instead of
+        // a 64-bit address (every offset is clamped into the row)
+        const __amdgpu_buffer_rsrc_t rin =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + (size_t)row * d), 0, d * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rout =
+            __builtin_amdgcn_make_buffer_rsrc(out + (size_t)row * d, 0, d * 2, 0x00020000);
+        u32x4 v[P];
 #pragma unroll
-        for (int i = 0; i < P; ++i) v[i] = src[min(lane + 64 * i, nvec - 1)];
+        for (int i = 0; i < P; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rin, 16 * min(lane + 64 * i, nvec - 1), 0, 0);
+        // Each pass below re-expands the packed pieces: the empty asm hides
+        // from the compiler that they are unchanged, so it does not keep 8
+        // floats per piece live from one pass to the next (which would not
+        // fit the register cap).
+        auto refresh = [&]() {
+#pragma unroll
+            for (int i = 0; i < P; ++i) asm volatile("" : "+v"(v[i]));
+        };
 
         float mean = 0.f, r = 1.f;
         if (NORM == NORM_LN) {
@@ -70,6 +81,7 @@ __global__ __launch_bounds__(256) void norm_rows_kernel(const uint16_t* x, int M
                 s += lane + 64 * i < nvec ? t : 0.f;
             }
             mean = wave_sum(s) * inv_d;
+            refresh();
             float dev = 0.f;
 #pragma unroll
             for (int i = 0; i < P; ++i) {
@@ -99,35 +111,35 @@ __global__ __launch_bounds__(256) void norm_rows_kernel(const uint16_t* x, int M
             r = 1.0f / sqrtf(wave_sum(sq) * inv_d + eps);
         }
 
-        uint4* dst = reinterpret_cast<uint4*>(out + (size_t)row * d);
+        refresh();
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             const int vi = min(lane + 64 * i, nvec - 1);
             if (NORM == NORM_NONE) {
-                dst[vi] = make_uint4(v[i].x, v[i].y, v[i].z, v[i].w);
+                __builtin_amdgcn_raw_buffer_store_b128(v[i], rout, 16 * vi, 0, 0);
             } else {
-                const float4* g4 = reinterpret_cast<const float4*>(gb + 8 * vi);
-                const float4* b4 = reinterpret_cast<const float4*>(gb + d + 8 * vi);
-                const float4 g0 = g4[0], g1 = g4[1], b0 = b4[0], b1 = b4[1];
-                const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-                const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                const u32x4 gw = gb[vi], bw = gb[nvec + vi];
                 const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
                 uint32_t o[4];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float lo = (bf_lo(w[q]) - mean) * r * g[2 * q] + b[2 * q];
-                    const float hi = (bf_hi(w[q]) - mean) * r * g[2 * q + 1] + b[2 * q + 1];
+                    const float lo = (bf_lo(w[q]) - mean) * r * bf_lo(gw[q]) + bf_lo(bw[q]);
+                    const float hi = (bf_hi(w[q]) - mean) * r * bf_hi(gw[q]) + bf_hi(bw[q]);
                     o[q] = pack_bf2(lo, hi);
                 }
-                dst[vi] = make_uint4(o[0], o[1], o[2], o[3]);
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, rout, 16 * vi, 0, 0);
             }
+            // one piece at a time: hoisting every piece's gamma / beta reads
+            // would not fit the register cap
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
-// Workgroups: enough for every row, at most 512 (two per CU, which is what
-// 8*d bytes of LDS at d = 8192 allow); each wave then takes rows at a stride
-// of 4 * grid.
+// Workgroups: enough for every row, at most 512 (two per CU, the four waves
+// per SIMD the register cap allows); each wave then takes rows at a stride of
+// 8 * grid.  P is the smallest listed piece count that covers the row, exact
+// for d = 512 * P.
 template <int NORM>
 static hipError_t launch_norm_rows_p(const uint16_t* x, int M, int d, float eps, const uint16_t* gamma,
                                      const uint16_t* beta, uint16_t* out, hipStream_t st) {
@@ -136,15 +148,20 @@ static hipError_t launch_norm_rows_p(const uint16_t* x, int M, int d, float eps,
     const uint16_t* gp = has_g ? gamma : x;
     const uint16_t* bp = has_b ? beta : x;
     const int nvec = d / 8;
-    const int grid = (int)std::min<int64_t>(((int64_t)M + 3) / 4, 512);
-    const size_t lds = NORM == NORM_NONE ? 0 : (size_t)d * 2 * sizeof(float);
+    const int grid = (int)std::min<int64_t>(((int64_t)M + NR_WAVES - 1) / NR_WAVES, 512);
+    const size_t lds = NORM == NORM_NONE ? 0 : (size_t)d * 2 * sizeof(uint16_t);
 #define E31_NORM_ROWS(PP) \
-    norm_rows_kernel<NORM, PP><<<grid, 256, lds, st>>>(x, M, d, eps, gp, has_g, bp, has_b, out)
-    if (nvec <= 64) E31_NORM_ROWS(1);
-    else if (nvec <= 128) E31_NORM_ROWS(2);
-    else if (nvec <= 256) E31_NORM_ROWS(4);
-    else if (nvec <= 512) E31_NORM_ROWS(8);
-    else if (nvec <= 768) E31_NORM_ROWS(12);
+    norm_rows_kernel<NORM, PP><<<grid, 64 * NR_WAVES, lds, st>>>(x, M, d, eps, gp, has_g, bp, has_b, out)
+    const int need = (nvec + 63) / 64;
+    if (need <= 1) E31_NORM_ROWS(1);
+    else if (need <= 2) E31_NORM_ROWS(2);
+    else if (need <= 3) E31_NORM_ROWS(3);
+    else if (need <= 4) E31_NORM_ROWS(4);
+    else if (need <= 6) E31_NORM_ROWS(6);
+    else if (need <= 8) E31_NORM_ROWS(8);
+    else if (need <= 10) E31_NORM_ROWS(10);
+    else if (need <= 12) E31_NORM_ROWS(12);
+    else if (need <= 14) E31_NORM_ROWS(14);
     else E31_NORM_ROWS(16);
 #undef E31_NORM_ROWS
     return hipGetLastError();
