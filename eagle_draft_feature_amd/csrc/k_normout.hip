@@ -29,6 +29,7 @@
 namespace e31 {
 
 constexpr int NR_WAVES = 8;
+constexpr int NT = 2;  // buffer instruction cache policy: non-temporal
 
 template <int NORM, int P>
 __global__ __launch_bounds__(64 * NR_WAVES) __attribute__((amdgpu_waves_per_eu(4))) void norm_rows_kernel(const uint16_t* x, int M, int d, float eps,
@@ -52,14 +53,16 @@ __global__ __launch_bounds__(64 * NR_WAVES) __attribute__((amdgpu_waves_per_eu(4
     const int nwaves = gridDim.x * NR_WAVES;
     for (int row = blockIdx.x * NR_WAVES + (threadIdx.x >> 6); row < M; row += nwaves) {
         // buffer accesses over the row: one 32-bit offset per piece instead of
-        // a 64-bit address (every offset is clamped into the row)
+        // a 64-bit address (every offset is clamped into the row).  Loads and
+        // stores carry the non-temporal hint (cache policy bit 1): every byte
+        // is touched once.
         const __amdgpu_buffer_rsrc_t rin =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x + (size_t)row * d), 0, d * 2, 0x00020000);
         const __amdgpu_buffer_rsrc_t rout =
             __builtin_amdgcn_make_buffer_rsrc(out + (size_t)row * d, 0, d * 2, 0x00020000);
         u32x4 v[P];
 #pragma unroll
-        for (int i = 0; i < P; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rin, 16 * min(lane + 64 * i, nvec - 1), 0, 0);
+        for (int i = 0; i < P; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rin, 16 * min(lane + 64 * i, nvec - 1), 0, NT);
         // Each pass below re-expands the packed pieces: the empty asm hides
         // from the compiler that they are unchanged, so it does not keep 8
         // floats per piece live from one pass to the next (which would not
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(64 * NR_WAVES) __attribute__((amdgpu_waves_per_eu(4
         for (int i = 0; i < P; ++i) {
             const int vi = min(lane + 64 * i, nvec - 1);
             if (NORM == NORM_NONE) {
-                __builtin_amdgcn_raw_buffer_store_b128(v[i], rout, 16 * vi, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(v[i], rout, 16 * vi, 0, NT);
             } else {
                 const u32x4 gw = gb[vi], bw = gb[nvec + vi];
                 const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(64 * NR_WAVES) __attribute__((amdgpu_waves_per_eu(4
                     const float hi = (bf_hi(w[q]) - mean) * r * bf_hi(gw[q]) + bf_hi(bw[q]);
                     o[q] = pack_bf2(lo, hi);
                 }
-                __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, rout, 16 * vi, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[0], o[1], o[2], o[3]}, rout, 16 * vi, 0, NT);
             }
             // one piece at a time: hoisting every piece's gamma / beta reads
             // would not fit the register cap
