@@ -50,6 +50,22 @@
 
 namespace e31 {
 
+// A W row piece with the non-temporal hint: the stored weight is read once
+// per call (the hidden-state rows, re-read across column groups, are not).
+template <typename T>
+__device__ __forceinline__ T load_w_nt(const uint16_t* p);
+template <>
+__device__ __forceinline__ uint4 load_w_nt<uint4>(const uint16_t* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+template <>
+__device__ __forceinline__ uint2 load_w_nt<uint2>(const uint16_t* p) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return make_uint2(v[0], v[1]);
+}
+
 constexpr int DW = 8;                           // waves per workgroup
 constexpr int DTHREADS = 64 * DW;
 constexpr int DECODE_MAX_KS = 8;                // K chunks per column block
@@ -191,7 +207,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
         if (t < tp1) {
             const uint16_t* wp = wbase + (size_t)t * wstep;
 #pragma unroll
-            for (int r = 0; r < NL; ++r) wr[r] = *reinterpret_cast<const LT*>(wp + (size_t)r * wsub);
+            for (int r = 0; r < NL; ++r) wr[r] = load_w_nt<LT>(wp + (size_t)r * wsub);
         }
         for (; t < tp1; t += DW) {
             const int k = t * 32;
@@ -229,7 +245,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
                 const int tn = (t + DW) < tp1 ? t + DW : t;
                 const uint16_t* wp = wbase + (size_t)tn * wstep;
 #pragma unroll
-                for (int r = 0; r < NL; ++r) wr[r] = *reinterpret_cast<const LT*>(wp + (size_t)r * wsub);
+                for (int r = 0; r < NL; ++r) wr[r] = load_w_nt<LT>(wp + (size_t)r * wsub);
             }
             __builtin_amdgcn_sched_barrier(0);
 
@@ -551,7 +567,7 @@ __global__ __launch_bounds__(512) void decode_one_kernel(DecodeArgs a) {
     const int nsteps = rows / 8;     // a multiple of R
     uint4 rw[R];
 #pragma unroll
-    for (int p = 0; p < R; ++p) rw[p] = *reinterpret_cast<const uint4*>(wp + (size_t)p * wstep);
+    for (int p = 0; p < R; ++p) rw[p] = load_w_nt<uint4>(wp + (size_t)p * wstep);
 
     // statistics of the three rows (waves 0..2)
     if (NORM != NORM_NONE && wave < 3) {
@@ -607,7 +623,7 @@ __global__ __launch_bounds__(512) void decode_one_kernel(DecodeArgs a) {
 #pragma unroll
         for (int p = 0; p < R; ++p) {
             fma_row(rw[p], xr[(i + p) * 8]);
-            rw[p] = *reinterpret_cast<const uint4*>(wp + (size_t)(i + p + R) * wstep);
+            rw[p] = load_w_nt<uint4>(wp + (size_t)(i + p + R) * wstep);
             __builtin_amdgcn_sched_barrier(0);
         }
     }

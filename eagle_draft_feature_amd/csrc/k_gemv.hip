@@ -11,6 +11,8 @@
 // W' is stored as 1 KiB tiles in MFMA B-fragment order (16 columns x 32 k,
 // lane l's 8 values at bytes [16 l, 16 l + 16)), the tiles of one 16-column
 // block consecutive along k, so a wave's W' load is one contiguous 1 KiB.
+// W' is read once per call, so its loads carry the non-temporal hint; the
+// hidden-state tiles, re-read by every column group, are ordinary loads.
 //
 // Work split: workgroup = 64 or 128 columns (4 or 8 column blocks) x one K
 // chunk inside one state, so each A fragment feeds 4 or 8 MFMAs from
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
     u32x4 rx[RA][MT];
     auto wload = [&](int i, u32x4 (&w)[NB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b) w[b] = wp[(size_t)b * wblk + (size_t)i * wstep];
+        for (int b = 0; b < NB; ++b) w[b] = __builtin_nontemporal_load(&wp[(size_t)b * wblk + (size_t)i * wstep]);
     };
     auto aload = [&](int i, u32x4 (&x)[MT]) __attribute__((always_inline)) {
 #pragma unroll
@@ -540,7 +542,7 @@ __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
     constexpr int WSTEP = WH_WAVES * 64;  // uint4 between a wave's steps
     u32x4 rw[R];
 #pragma unroll
-    for (int p = 0; p < R; ++p) rw[p] = wp[(size_t)p * WSTEP];
+    for (int p = 0; p < R; ++p) rw[p] = __builtin_nontemporal_load(&wp[(size_t)p * WSTEP]);
 
     // token rows into LDS, states concatenated (row m: k = 0 .. 3d-1)
     {
@@ -612,7 +614,7 @@ __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
                 const int jj = j0 + i + p;
                 const u32x4 af = *reinterpret_cast<const u32x4*>(abase + (wave + WH_WAVES * jj) * 64);
                 ac = mfma16x16x32(af, rw[p], ac);
-                rw[p] = wp[(size_t)(jj + R) * WSTEP];
+                rw[p] = __builtin_nontemporal_load(&wp[(size_t)(jj + R) * WSTEP]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
