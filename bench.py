@@ -50,7 +50,7 @@ def parse():
     p.add_argument("--no-sweep", action="store_true", help="skip the per-M decode sweep")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurements")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
-    p.add_argument("--only", choices=["decode", "decode_folded", "prefill", "rowstats", "copy", "postnorm"], default=None,
+    p.add_argument("--only", choices=["decode", "decode_folded", "prefill", "rowstats", "copy", "postnorm", "postnorm_decode"], default=None,
                    help="run a single leg (used under rocprofv3)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
@@ -343,6 +343,9 @@ def main():
         return
     if args.only == "prefill":
         print(json.dumps(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, max(3, args.steps), args.warmup, folded=True)))
+        return
+    if args.only == "postnorm_decode":
+        print(json.dumps(postnorm_leg(torch, pkg, synth, 2, 64, 1, 1e-5, max(50, args.steps), args.warmup)))
         return
     if args.only == "postnorm":
         print(json.dumps(postnorm_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, max(5, args.steps), args.warmup)))
