@@ -129,3 +129,17 @@ def test_norm_output_prefill_shape_sampled():
     rows = sample_rows(32768, k=96, seed=3)
     Y = oracle.norm_output_bits(x[rows], LN, 1e-5, g, b)
     assert_elementwise(G[rows], Y, "norm_output prefill sampled")
+
+
+@pytest.mark.parametrize("kind", [LN, RMS])
+def test_norm_output_grid_stride_ragged(kind):
+    """More rows than the grid has waves (512 workgroups x 8 waves), at a
+    ragged width (1088: the last round of pieces has 8 lanes): every wave
+    takes two rows, some of its lanes re-read and re-write a clamped piece.
+    Every row against the oracle."""
+    print(f"[case] norm_output grid stride d=1088 M=4500 kind={kind}", flush=True)
+    x, g, b = rows_of(1088, 4500, seed_tag=23)
+    eps = 1e-5 if kind == LN else 1e-6
+    G = bf16_to_f64(run(x, kind, eps, g, b))
+    Y = oracle.norm_output_bits(x, kind, eps, g, b if kind == LN else None)
+    assert_elementwise(G, Y, f"norm_output grid stride kind={kind}")
