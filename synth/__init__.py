@@ -8,7 +8,7 @@ computation.
 """
 
 from .workloads import CONFIGS, Workload, workload
-from .gen import Inputs, make_inputs, bf16_round, bf16_bits, bits_to_f32
+from .gen import Inputs, make_inputs, make_embed_inputs, bf16_round, bf16_bits, bits_to_f32
 
 __all__ = [
     "CONFIGS",
@@ -16,6 +16,7 @@ __all__ = [
     "workload",
     "Inputs",
     "make_inputs",
+    "make_embed_inputs",
     "bf16_round",
     "bf16_bits",
     "bits_to_f32",

@@ -172,3 +172,20 @@ def custom_workload(d: int, Ms, seed_tag: int, *, scales=(1.0, 4.0, 16.0), offse
     """
     return Workload(1000 + seed_tag, f"custom{seed_tag}_d{d}", d, tuple(Ms), tuple(norms), tuple(scales),
                     tuple(offset_std), n_outliers, outlier_mult, has_beta, has_bias)
+
+
+def make_embed_inputs(M: int, d: int, vocab: int, seed: int, n_bad: int = 0):
+    """Inputs of the drafter-input concatenation: token ids int32 [M] uniform
+    over [0, vocab), of which n_bad spread positions are replaced by ids
+    outside the table (alternately -1 - k and vocab + k); an embedding table
+    bf16 [vocab, d] ~ N(0, 0.02); a fused feature bf16 [M, d] ~ N(0, 1).
+    Returns (tokens, embed_bits, fused_bits)."""
+    s_tok, s_emb, s_fus = np.random.SeedSequence(seed).spawn(3)
+    tokens = np.random.Generator(np.random.PCG64(s_tok)).integers(0, vocab, size=M, dtype=np.int64)
+    for k, pos in enumerate(np.linspace(0, M - 1, num=min(n_bad, M), dtype=np.int64)):
+        tokens[pos] = -1 - k if k % 2 == 0 else vocab + k
+    rng_e = np.random.Generator(np.random.PCG64(s_emb))
+    embed = bf16_bits(rng_e.standard_normal((vocab, d), dtype=np.float32) * np.float32(0.02))
+    rng_f = np.random.Generator(np.random.PCG64(s_fus))
+    fused = bf16_bits(rng_f.standard_normal((M, d), dtype=np.float32))
+    return tokens.astype(np.int32), embed, fused

@@ -373,3 +373,38 @@ def check_norm_output_closed_forms(norm_fn, tol=1e-13) -> bool:
     ok &= np.allclose(norm_fn(a, NORM_LN, 1e-3, g, b), want + b, rtol=0, atol=tol)
     ok &= np.allclose(norm_fn(a, NORM_RMS, 1e-3, g, b), want, rtol=0, atol=tol)
     return bool(ok)
+
+
+# ---------------------------------------------------------------------------
+# Drafter-input concatenation: fn(tokens, embed_bits, fused_bits) -> (dst, bad)
+# ---------------------------------------------------------------------------
+
+
+def check_embed_concat_hand(fn) -> bool:
+    """A table of 3 rows of width 2 and 4 tokens, the result written by hand."""
+    embed = np.array([[1, 2], [3, 4], [5, 6]], dtype=np.uint16)
+    fused = np.array([[10, 11], [12, 13], [14, 15], [16, 17]], dtype=np.uint16)
+    tokens = np.array([2, 0, -1, 3], dtype=np.int32)
+    want = np.array([[5, 6, 10, 11], [1, 2, 12, 13], [0, 0, 14, 15], [0, 0, 16, 17]], dtype=np.uint16)
+    dst, bad = fn(tokens, embed, fused)
+    return bool(np.array_equal(dst, want) and bad == 2)
+
+
+def check_embed_concat_brute(fn, seed=31, M=9, d=5, vocab=4) -> bool:
+    """Element-by-element loops over a small case with ids inside and outside
+    the table."""
+    rng = np.random.default_rng(seed)
+    embed = rng.integers(1, 65535, size=(vocab, d)).astype(np.uint16)
+    fused = rng.integers(1, 65535, size=(M, d)).astype(np.uint16)
+    tokens = rng.integers(-2, vocab + 2, size=M).astype(np.int32)
+    dst, bad = fn(tokens, embed, fused)
+    nbad = 0
+    for m in range(M):
+        inside = 0 <= int(tokens[m]) < vocab
+        nbad += 0 if inside else 1
+        for j in range(d):
+            if dst[m, j] != (embed[int(tokens[m]), j] if inside else 0):
+                return False
+            if dst[m, d + j] != fused[m, j]:
+                return False
+    return bad == nbad and dst.shape == (M, 2 * d)

@@ -144,3 +144,35 @@ def test_postnorm_mutant_harness_is_faithful():
     """The unmutated copy passes every pin (so a failure above is the slip's)."""
     fn = _postnorm_mutant(None)
     assert pins.check_norm_output_torch(fn) and pins.check_norm_output_closed_forms(fn)
+
+
+# --- drafter-input concatenation: planted slips ---------------------------------
+
+
+def _embedcat_mutant(slip):
+    def fn(tokens, embed, fused):
+        tokens = np.asarray(tokens, dtype=np.int64)
+        vocab, d = embed.shape
+        ok = (tokens >= 0) & (tokens < vocab)
+        if slip == "clamp_ids":
+            left = embed[np.clip(tokens, 0, vocab - 1)]
+        else:
+            t = tokens + 1 if slip == "off_by_one" else tokens
+            ok2 = (t >= 0) & (t < vocab)
+            left = np.zeros((len(tokens), d), dtype=np.uint16)
+            left[ok2] = embed[t[ok2]]
+        parts = [fused, left] if slip == "swapped" else [left, fused]
+        bad = int(np.count_nonzero(~ok)) + (1 if slip == "count" else 0)
+        return np.concatenate(parts, axis=1), bad
+    return fn
+
+
+@pytest.mark.parametrize("slip", ["clamp_ids", "off_by_one", "swapped", "count"])
+def test_embedcat_mutants_fail_a_pin(slip):
+    fn = _embedcat_mutant(slip)
+    assert not (pins.check_embed_concat_hand(fn) and pins.check_embed_concat_brute(fn))
+
+
+def test_embedcat_mutant_harness_is_faithful():
+    fn = _embedcat_mutant(None)
+    assert pins.check_embed_concat_hand(fn) and pins.check_embed_concat_brute(fn)

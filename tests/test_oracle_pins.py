@@ -148,3 +148,11 @@ def test_norm_output_bits_decodes_like_fuse_inputs():
     want = oracle.norm_output(oracle.decode_bf16(inp.h[0]), oracle.NORM_LN, 1e-5, oracle.decode_bf16(inp.gamma[0]),
                               oracle.decode_bf16(inp.beta[0]))
     assert np.array_equal(got, want)
+
+
+def test_embed_concat_hand_example():
+    assert pins.check_embed_concat_hand(oracle.embed_concat)
+
+
+def test_embed_concat_brute_force():
+    assert pins.check_embed_concat_brute(oracle.embed_concat)
