@@ -50,7 +50,8 @@ def parse():
     p.add_argument("--no-sweep", action="store_true", help="skip the per-M decode sweep")
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurements")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
-    p.add_argument("--only", choices=["decode", "decode_folded", "prefill", "rowstats", "copy", "postnorm", "postnorm_decode"], default=None,
+    p.add_argument("--only", choices=["decode", "decode_folded", "prefill", "rowstats", "copy", "postnorm", "postnorm_decode",
+                                             "embedcat"], default=None,
                    help="run a single leg (used under rocprofv3)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
@@ -277,6 +278,33 @@ def postnorm_leg(torch, pkg, synth, cfg, M, kind, eps, steps, warmup):
     return res
 
 
+def embedcat_leg(torch, pkg, synth, M, d, steps, warmup, vocab=32000):
+    """eagle31_embed_concat on one workload's shape: an embedding row and a
+    fused row read, a [2d] row written per token; cold copies rotated."""
+    import numpy as np
+    tokens, embed, fused = synth.make_embed_inputs(M, d, vocab, seed=3)
+    foot = 3 * M * d * 2
+    R = 2 if foot >= MALL_BYTES else rotation_count(foot)
+    tok = torch.from_numpy(np.ascontiguousarray(tokens)).to("cuda")
+    emb = to_dev(embed)
+    f0 = to_dev(fused)
+    fs = [f0] + [f0.clone() for _ in range(R - 1)]
+    outs = [torch.empty((M, 2 * d), dtype=torch.bfloat16, device="cuda") for _ in range(R)]
+
+    def fn(i):
+        pkg.embed_concat(tok, emb, fs[i], out=outs[i])
+
+    t, _ = time_loop(torch, fn, R, steps, warmup)
+    per = t / steps
+    nbytes = 4 * M * d * 2 + 4 * M  # embedding rows + fused rows read, [M, 2d] written, token ids
+    res = dict(entry="eagle31_embed_concat", kernel="embed_concat_kernel", d=d, M=M, vocab=vocab, steps=steps, R=R,
+               us_per_call=round(per * 1e6, 3), bytes_per_call=nbytes, gbs=round(nbytes / per / 1e9, 1),
+               hbm_frac=round(nbytes / per / 1e9 / HBM_PEAK_GBS, 4))
+    del fs, outs, emb
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline_leg(inp, kind, eps, budget_s):
     """The fp64 oracle as it stands, on preconverted float64 arrays, repeated
     until about budget_s seconds of host work."""
@@ -343,6 +371,10 @@ def main():
         return
     if args.only == "prefill":
         print(json.dumps(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, max(3, args.steps), args.warmup, folded=True)))
+        return
+    if args.only == "embedcat":
+        print(json.dumps([embedcat_leg(torch, pkg, synth, 64, 4096, max(50, args.steps), args.warmup),
+                          embedcat_leg(torch, pkg, synth, 32768, 7168, 20, 5)]))
         return
     if args.only == "postnorm_decode":
         print(json.dumps(postnorm_leg(torch, pkg, synth, 2, 64, 1, 1e-5, max(50, args.steps), args.warmup)))
@@ -418,6 +450,12 @@ def main():
     if not args.no_prefill:
         postnorm.append(postnorm_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, 20, 5))
 
+    # the drafter-input concatenation (embedding of the last token, then the
+    # fused feature) at the decode and prefill shapes
+    embedcat = [embedcat_leg(torch, pkg, synth, 64, 4096, 400, 50)]
+    if not args.no_prefill:
+        embedcat.append(embedcat_leg(torch, pkg, synth, 32768, 7168, 20, 5))
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline_leg(dec["inp"], dec["kind"], dec["eps"], args.cpu_seconds)
@@ -446,6 +484,7 @@ def main():
         "prefill": prefill,
         "other_workloads": others,
         "postnorm": postnorm,
+        "embed_concat": embedcat,
     }
     print(json.dumps(line))
 

@@ -475,6 +475,26 @@ int eagle31_norm_output(const void* x, int64_t M, int64_t d, int norm_kind, floa
     return EAGLE31_OK;
 }
 
+int eagle31_embed_concat(const int32_t* tokens, int64_t M, int64_t d, int64_t vocab, const void* embed,
+                         const void* fused, void* dst, int32_t* bad_count, void* stream) {
+    if (M < 0 || M > MAX_M || d <= 0 || d > EMBED_CONCAT_MAX_D || (d % 64) != 0 || vocab < 1 || vocab > INT32_MAX)
+        return EAGLE31_ERR_SHAPE;
+    if (M == 0) return EAGLE31_OK;
+    if (tokens == nullptr || embed == nullptr || fused == nullptr || dst == nullptr) return EAGLE31_ERR_NULL;
+    if (!aligned16(embed) || !aligned16(fused) || !aligned16(dst) || ((uintptr_t)tokens & 3u) != 0 ||
+        ((uintptr_t)bad_count & 3u) != 0)
+        return EAGLE31_ERR_ALIGN;
+    const size_t db = (size_t)M * (size_t)d * 4, rb = (size_t)M * (size_t)d * 2;
+    if (overlaps(dst, db, tokens, (size_t)M * 4) || overlaps(dst, db, embed, (size_t)vocab * (size_t)d * 2) ||
+        overlaps(dst, db, fused, rb) || overlaps(dst, db, bad_count, 4))
+        return EAGLE31_ERR_ALIAS;
+    const hipError_t e = launch_embed_concat(tokens, (int)M, (int)d, (int)vocab, static_cast<const uint16_t*>(embed),
+                                             static_cast<const uint16_t*>(fused), static_cast<uint16_t*>(dst),
+                                             bad_count, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return EAGLE31_OK;
+}
+
 const char* eagle31_status_string(int status) {
     switch (status) {
         case EAGLE31_OK: return "ok";

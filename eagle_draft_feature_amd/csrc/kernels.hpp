@@ -13,6 +13,11 @@ constexpr int NORM_ROWS_MAX_D = 8192;
 hipError_t launch_norm_rows(const uint16_t* x, int M, int d, int norm, float eps, const uint16_t* gamma,
                             const uint16_t* beta, uint16_t* out, hipStream_t st);
 
+// Drafter-input concatenation (dst[m] = [embed[tokens[m]] | fused[m]]).
+constexpr int EMBED_CONCAT_MAX_D = 8192;
+hipError_t launch_embed_concat(const int32_t* tokens, int M, int d, int vocab, const uint16_t* embed,
+                               const uint16_t* fused, uint16_t* dst, int32_t* bad_count, hipStream_t st);
+
 hipError_t launch_row_stats(const uint16_t* h0, const uint16_t* h1, const uint16_t* h2, int M, int d, int norm,
                             float eps, float* mu, float* rstd, hipStream_t st);
 

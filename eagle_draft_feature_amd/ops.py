@@ -197,6 +197,30 @@ def norm_output(x, norm, eps, gamma=None, beta=None, out=None):
     return out
 
 
+def embed_concat(tokens, embed, fused, out=None, bad_count=None):
+    """eagle31_embed_concat: [embed[tokens[m]] | fused[m]] per row -> bf16
+    [M, 2d].  tokens int32 [M]; bad_count: optional int32 [1] device tensor
+    that counts token ids outside the table (the caller zeroes it)."""
+    if (not isinstance(tokens, torch.Tensor) or tokens.dtype != torch.int32 or tokens.dim() != 1 or not tokens.is_cuda
+            or not tokens.is_contiguous()):
+        raise TypeError("tokens must be a contiguous 1-d int32 tensor on a GPU")
+    _want(embed, "embed", device=tokens.device)
+    if embed.dim() != 2:
+        raise ValueError("embed must be [vocab, d]")
+    vocab, d = embed.shape
+    M = tokens.shape[0]
+    _want(fused, "fused", shape=(M, d), device=tokens.device)
+    if out is None:
+        out = torch.empty((M, 2 * d), dtype=torch.bfloat16, device=tokens.device)
+    _want(out, "out", shape=(M, 2 * d), device=tokens.device)
+    if bad_count is not None and (bad_count.dtype != torch.int32 or bad_count.numel() != 1 or not bad_count.is_cuda):
+        raise TypeError("bad_count must be a one-element int32 tensor on a GPU")
+    st = lib().eagle31_embed_concat(_ptr(tokens), M, d, vocab, _ptr(embed), _ptr(fused), _ptr(out), _ptr(bad_count),
+                                    _stream(fused))
+    check("eagle31_embed_concat", st)
+    return out
+
+
 def release() -> None:
     check("eagle31_release", lib().eagle31_release())
 

@@ -187,6 +187,26 @@ int eagle31_row_stats(const void* h_low, const void* h_mid, const void* h_high, 
 int eagle31_norm_output(const void* x, int64_t M, int64_t d, int norm_kind, float eps, const void* gamma,
                         const void* beta, void* out, void* stream);
 
+/*
+ * eagle31_embed_concat - the drafter's input row: the embedding of the token
+ * sampled just before, followed by the fused feature (EAGLE-3 paper summary,
+ * honbul.tistory.com/173, section "EAGLE-3가 바꾼 것 2"):
+ *
+ *     dst[m, 0:d]  = embed[tokens[m], :]       (zeros if tokens[m] < 0 or >= vocab)
+ *     dst[m, d:2d] = fused[m, :]
+ *
+ * tokens:    int32 [M], device, 4-byte aligned.
+ * embed:     bf16 [vocab, d] row-major; fused: bf16 [M, d] (e.g. the output of
+ *            eagle31_fuse); dst: bf16 [M, 2d]; all 16-byte aligned.
+ * bad_count: device int32 or NULL; incremented once per token outside the
+ *            table (the caller zeroes it).  Such a token never faults.
+ * Bits are copied, nothing is rounded.  dst must not overlap any input.
+ * Limits: 1 <= vocab <= 2^31 - 1, d % 64 == 0, d <= 8192 (EAGLE31_ERR_SHAPE);
+ * M == 0 launches nothing.  Needs no scratch memory.
+ */
+int eagle31_embed_concat(const int32_t* tokens, int64_t M, int64_t d, int64_t vocab, const void* embed,
+                         const void* fused, void* dst, int32_t* bad_count, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* eagle31_status_string(int status);
 

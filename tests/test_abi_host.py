@@ -180,3 +180,32 @@ def test_norm_output_host_rules_for_parameters():
     assert _norm_out(M=0) == _capi.OK
     assert _norm_out(M=0, x=None, out=None) == _capi.OK
     assert _norm_out(M=0, norm=2, b=BP + 2, d=8192 + 64) == _capi.ERR_SHAPE
+
+
+def _ecat(tok=0x700000, M=64, d=4096, vocab=16, e=WP, f=H1, dst=OUT, bad=None):
+    # regions: embed [WP, WP + 128 KiB), fused [H1, H1 + 512 KiB), dst [OUT, OUT + 1 MiB), tokens at 0x700000
+    return e31.lib().eagle31_embed_concat(tok, M, d, vocab, e, f, dst, bad, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=8192 + 64), _capi.ERR_SHAPE),
+    (dict(d=96), _capi.ERR_SHAPE),
+    (dict(vocab=0), _capi.ERR_SHAPE),
+    (dict(vocab=2 ** 31), _capi.ERR_SHAPE),
+    (dict(M=-1), _capi.ERR_SHAPE),
+    (dict(tok=None), _capi.ERR_NULL),
+    (dict(e=None), _capi.ERR_NULL),
+    (dict(f=None), _capi.ERR_NULL),
+    (dict(dst=None), _capi.ERR_NULL),
+    (dict(tok=0x700002), _capi.ERR_ALIGN),
+    (dict(bad=0x700001), _capi.ERR_ALIGN),
+    (dict(e=WP + 8), _capi.ERR_ALIGN),
+    (dict(dst=OUT + 4), _capi.ERR_ALIGN),
+    (dict(dst=H1 - 1024), _capi.ERR_ALIAS),  # dst runs into the fused feature
+    (dict(tok=OUT + 64), _capi.ERR_ALIAS),
+    (dict(bad=OUT + 1024), _capi.ERR_ALIAS),
+    (dict(M=0, tok=None, dst=None), _capi.OK),
+    (dict(e=OUT + 4096 * 2 * 4), _capi.ERR_ALIAS),  # the table starts inside dst
+])
+def test_embed_concat_rejects_bad_arguments(kw, code):
+    assert _ecat(**kw) == code
