@@ -9,8 +9,10 @@ from .fuse64 import (NORM_LN, NORM_NONE, NORM_RMS, decode_bf16, fold_apply, fold
                      fuse_bits, normalize, round_bf16_rne, row_stats)
 from .postnorm64 import norm_output, norm_output_bits
 from .embedcat import embed_concat
+from .verify64 import inverse_cdf, verify_accept
 
 __all__ = [
     "NORM_NONE", "NORM_LN", "NORM_RMS", "decode_bf16", "row_stats", "normalize", "fuse", "fuse_bits",
     "fold_prepare", "fold_apply", "round_bf16_rne", "norm_output", "norm_output_bits", "embed_concat",
+    "inverse_cdf", "verify_accept",
 ]

@@ -408,3 +408,72 @@ def check_embed_concat_brute(fn, seed=31, M=9, d=5, vocab=4) -> bool:
             if dst[m, d + j] != fused[m, j]:
                 return False
     return bad == nbad and dst.shape == (M, 2 * d)
+
+
+# ---------------------------------------------------------------------------
+# Verify / accept: fn(p, q, draft, u_acc, u_res) -> (n_accepted, next_token)
+# ---------------------------------------------------------------------------
+
+
+def check_verify_hand(fn) -> bool:
+    """Worked by hand.  p_1 = (.5, .3, .2), q_1 = (.2, .5, .3): the draft 0 is
+    kept when u < .4.  Residual (q_1 - p_1)+ = (0, .2, .1), total .3: u_res = .5
+    aims at .15 -> token 1, u_res = .9 aims at .27 -> token 2.  A second draft
+    (token 2, p_2 = (.6, .2, .2), q_2 = (.2, .2, .6): ratio 3, always kept) is
+    never reached after a rejection at position 1.  All kept: the bonus from
+    q_3 = (.1, .1, .8) with u_res = .5 aims at .5 -> token 2."""
+    p = np.array([[[.5, .3, .2], [.6, .2, .2]]], dtype=np.float32)
+    q = np.array([[[.2, .5, .3], [.2, .2, .6], [.1, .1, .8]]], dtype=np.float32)
+    draft = np.array([[0, 2]])
+    cases = [((.5, .1), .5, 0, 1), ((.5, .1), .9, 0, 2), ((.3, .1), .5, 2, 2), ((.3, .1), .05, 2, 0)]
+    for ua, ur, n_want, t_want in cases:
+        n, t = fn(p, q, draft, np.array([ua], dtype=np.float32), np.array([ur], dtype=np.float32))
+        if int(n[0]) != n_want or int(t[0]) != t_want:
+            return False
+    return True
+
+
+def check_verify_q_equals_p(fn, seed=41, B=64, N=4, V=50) -> bool:
+    """With q = p every ratio is 1 > u, so all N drafts are kept and the
+    bonus comes from q_{N+1} by inverse CDF (brute-force loop here)."""
+    rng = np.random.default_rng(seed)
+    p = rng.dirichlet(np.ones(V), size=(B, N)).astype(np.float32)
+    q = np.concatenate([p, rng.dirichlet(np.ones(V), size=(B, 1)).astype(np.float32)], axis=1)
+    draft = rng.integers(0, V, size=(B, N))
+    u_acc = rng.random((B, N), dtype=np.float32)
+    u_res = rng.random(B, dtype=np.float32)
+    n, t = fn(p, q, draft, u_acc, u_res)
+    if not np.all(n == N):
+        return False
+    for b in range(B):
+        w = q[b, N].astype(np.float64)
+        target, run, pick = float(u_res[b]) * w.sum(), 0.0, V - 1
+        for k in range(V):
+            run += w[k]
+            if run > target:
+                pick = k
+                break
+        if int(t[b]) != pick:
+            return False
+    return True
+
+
+def check_verify_leviathan(fn, seed=43, B=50000, V=8, alpha=1e-6) -> bool:
+    """The invariant the pages state: the emitted token follows q whatever p
+    is.  50,000 seeded single-draft steps (draft ~ p); the first emitted token
+    (the draft if kept, else the residual's) is chi-square tested against q."""
+    from scipy.stats import chi2
+
+    rng = np.random.default_rng(seed)
+    pr = rng.dirichlet(np.ones(V) * 0.7).astype(np.float32)
+    qr = rng.dirichlet(np.ones(V) * 0.7).astype(np.float32)
+    p = np.broadcast_to(pr, (B, 1, V))
+    q = np.broadcast_to(qr, (B, 2, V))
+    cdf = np.cumsum(pr.astype(np.float64))
+    draft = np.minimum(np.searchsorted(cdf, rng.random(B) * cdf[-1], side="right"), V - 1)[:, None]
+    n, t = fn(p, q, draft, rng.random((B, 1), dtype=np.float32), rng.random(B, dtype=np.float32))
+    first = np.where(n == 1, draft[:, 0], t)
+    counts = np.bincount(first, minlength=V)
+    expect = qr.astype(np.float64) / qr.sum() * B
+    stat = float(((counts - expect) ** 2 / expect).sum())
+    return bool(chi2.sf(stat, V - 1) > alpha)

@@ -176,3 +176,55 @@ def test_embedcat_mutants_fail_a_pin(slip):
 def test_embedcat_mutant_harness_is_faithful():
     fn = _embedcat_mutant(None)
     assert pins.check_embed_concat_hand(fn) and pins.check_embed_concat_brute(fn)
+
+
+# --- verify / accept: planted slips ---------------------------------------------
+
+
+def _verify_mutant(slip):
+    import oracle.verify64 as v
+
+    def fn(p, q, draft, u_acc, u_res):
+        p = np.asarray(p, dtype=np.float32)
+        q = np.asarray(q, dtype=np.float32)
+        B, N, V = p.shape
+        n_acc = np.zeros(B, dtype=np.int32)
+        nxt = np.zeros(B, dtype=np.int32)
+        for b in range(B):
+            j, rejected = N, False
+            for i in range(N):
+                pd, qd = p[b, i, draft[b, i]], q[b, i, draft[b, i]]
+                ratio = pd / qd if slip == "inverted_ratio" else qd / pd
+                if not (pd <= 0 or u_acc[b, i] < min(np.float32(1), np.float32(ratio))):
+                    if not rejected:
+                        j, rejected = i, True
+                    if slip != "no_stop":
+                        break
+                elif slip == "no_stop" and rejected:
+                    j += 1
+            n_acc[b] = j
+            if j < N:
+                if slip == "flipped_residual":
+                    w = np.maximum(p[b, j] - q[b, j], 0)
+                elif slip == "unclipped":
+                    w = np.abs(q[b, j] - p[b, j])
+                else:
+                    w = np.maximum(q[b, j] - p[b, j], 0)
+                if not np.any(w > 0):
+                    w = q[b, j]
+            else:
+                w = q[b, N - 1 if slip == "bonus_row" else N]
+            nxt[b] = v.inverse_cdf(w, u_res[b])
+        return n_acc, nxt
+    return fn
+
+
+@pytest.mark.parametrize("slip", ["inverted_ratio", "flipped_residual", "unclipped", "bonus_row", "no_stop"])
+def test_verify_mutants_fail_a_pin(slip):
+    fn = _verify_mutant(slip)
+    assert not (pins.check_verify_hand(fn) and pins.check_verify_q_equals_p(fn) and pins.check_verify_leviathan(fn))
+
+
+def test_verify_mutant_harness_is_faithful():
+    fn = _verify_mutant(None)
+    assert pins.check_verify_hand(fn) and pins.check_verify_q_equals_p(fn) and pins.check_verify_leviathan(fn)

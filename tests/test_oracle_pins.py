@@ -156,3 +156,18 @@ def test_embed_concat_hand_example():
 
 def test_embed_concat_brute_force():
     assert pins.check_embed_concat_brute(oracle.embed_concat)
+
+
+def test_verify_hand_example():
+    import oracle.verify64 as v
+    assert pins.check_verify_hand(v.verify_accept)
+
+
+def test_verify_q_equals_p_keeps_everything():
+    import oracle.verify64 as v
+    assert pins.check_verify_q_equals_p(v.verify_accept)
+
+
+def test_verify_emitted_token_follows_q():
+    import oracle.verify64 as v
+    assert pins.check_verify_leviathan(v.verify_accept)
