@@ -458,10 +458,14 @@ def check_verify_q_equals_p(fn, seed=41, B=64, N=4, V=50) -> bool:
     return True
 
 
-def check_verify_leviathan(fn, seed=43, B=50000, V=8, alpha=1e-6) -> bool:
+def check_verify_leviathan(fn, seed=43, B=50000, V=8, alpha=0.05) -> bool:
     """The invariant the pages state: the emitted token follows q whatever p
     is.  50,000 seeded single-draft steps (draft ~ p); the first emitted token
-    (the draft if kept, else the residual's) is chi-square tested against q."""
+    (the draft if kept, else the residual's) must pass, at the 95% critical
+    value the lesson's exercise uses (section "연습문제", exercise 1):
+    a chi-square goodness-of-fit test against q, and (section "직접 만들기",
+    Step 5) a two-sample test against 50,000 tokens drawn from q directly by
+    numpy's own sampler."""
     from scipy.stats import chi2
 
     rng = np.random.default_rng(seed)
@@ -469,11 +473,106 @@ def check_verify_leviathan(fn, seed=43, B=50000, V=8, alpha=1e-6) -> bool:
     qr = rng.dirichlet(np.ones(V) * 0.7).astype(np.float32)
     p = np.broadcast_to(pr, (B, 1, V))
     q = np.broadcast_to(qr, (B, 2, V))
-    cdf = np.cumsum(pr.astype(np.float64))
-    draft = np.minimum(np.searchsorted(cdf, rng.random(B) * cdf[-1], side="right"), V - 1)[:, None]
+    p64 = pr.astype(np.float64) / pr.astype(np.float64).sum()
+    draft = rng.choice(V, size=B, p=p64)[:, None]
     n, t = fn(p, q, draft, rng.random((B, 1), dtype=np.float32), rng.random(B, dtype=np.float32))
     first = np.where(n == 1, draft[:, 0], t)
-    counts = np.bincount(first, minlength=V)
-    expect = qr.astype(np.float64) / qr.sum() * B
-    stat = float(((counts - expect) ** 2 / expect).sum())
-    return bool(chi2.sf(stat, V - 1) > alpha)
+    if np.any(first < 0):
+        return False
+    counts = np.bincount(first, minlength=V).astype(np.float64)
+    q64 = qr.astype(np.float64) / qr.astype(np.float64).sum()
+    expect = q64 * B
+    stat_fit = float(((counts - expect) ** 2 / expect).sum())
+    direct = np.bincount(rng.choice(V, size=B, p=q64), minlength=V).astype(np.float64)
+    used = (counts + direct) > 0
+    stat_two = float(((counts[used] - direct[used]) ** 2 / (counts[used] + direct[used])).sum())
+    crit = chi2.ppf(1 - alpha, V - 1)
+    return stat_fit < crit and stat_two < chi2.ppf(1 - alpha, int(used.sum()) - 1)
+
+
+def check_verify_zero_probability_drafts(fn) -> bool:
+    """A draft the verifier gives zero probability is never kept, even when
+    the drafter also gave it zero (q(d) = p(d) = 0); one with p(d) = 0 and
+    q(d) > 0 is kept; an id outside the vocabulary is rejected.  After the
+    rejection of a zero-zero draft with q = p the residual is all zero and the
+    token comes from q itself (hand-worked: q = (.25, .75, 0), u_res = .5 aims
+    at .5 -> token 1)."""
+    p = np.array([[[.25, .75, 0.]]], dtype=np.float32)
+    qsame = np.array([[[.25, .75, 0.], [1., 0., 0.]]], dtype=np.float32)
+    qpos = np.array([[[.2, .5, .3], [0., 0., 1.]]], dtype=np.float32)
+    ua = np.array([[.5]], dtype=np.float32)
+    ur = np.array([.5], dtype=np.float32)
+    n, t = fn(p, qsame, np.array([[2]]), ua, ur)
+    if int(n[0]) != 0 or int(t[0]) != 1:
+        return False
+    n, t = fn(p, qpos, np.array([[2]]), ua, ur)          # kept, then the bonus from q_2 -> token 2
+    if int(n[0]) != 1 or int(t[0]) != 2:
+        return False
+    for bad in (-1, 3, 1 << 20):                           # outside the vocabulary: rejected
+        n, t = fn(p, qpos, np.array([[bad]]), ua, ur)
+        # residual (q - p)+ = (0, 0, .3) -> token 2
+        if int(n[0]) != 0 or int(t[0]) != 2:
+            return False
+    return True
+
+
+def check_verify_invalid_rows(fn) -> bool:
+    """No token (-1) when the weights sampled from are all zero, hold NaN or
+    a value above 1, or u_res is outside [0, 1)."""
+    p = np.array([[[.5, .5]]], dtype=np.float32)
+    ok = np.array([[.9]], dtype=np.float32)                 # .9 * .5 < .5 is false: rejected
+    keep = np.array([[.1]], dtype=np.float32)
+    cases = [
+        (np.array([[[.5, .5], [0., 0.]]], dtype=np.float32), keep, .5),          # bonus row all zero
+        (np.array([[[.5, .5], [np.nan, .5]]], dtype=np.float32), keep, .5),      # bonus row with NaN
+        (np.array([[[.5, .5], [2., .5]]], dtype=np.float32), keep, .5),          # bonus row above 1
+        (np.array([[[np.nan, .5], [.5, .5]]], dtype=np.float32), ok, .5),        # residual with NaN
+        (np.array([[[.5, .5], [.5, .5]]], dtype=np.float32), keep, 1.0),         # u_res = 1
+        (np.array([[[.5, .5], [.5, .5]]], dtype=np.float32), keep, -0.25),       # u_res < 0
+    ]
+    for q, ua, ur in cases:
+        _, t = fn(p, q, np.array([[0]]), ua, np.array([ur], dtype=np.float32))
+        if int(t[0]) != -1:
+            return False
+    return True
+
+
+def _inverse_cdf_fractions(w, u) -> int:
+    """Direct definition with rational arithmetic: smallest t with
+    w_0 + ... + w_t > u * total."""
+    from fractions import Fraction
+    ws = [Fraction(float(x)) for x in np.asarray(w, dtype=np.float32).tolist()]
+    target = Fraction(float(np.float32(u))) * sum(ws, Fraction(0))
+    run = Fraction(0)
+    for t, x in enumerate(ws):
+        run += x
+        if run > target:
+            return t
+    return -1
+
+
+def check_inverse_cdf_exact(fn_icdf, seed=47) -> bool:
+    """The emitted token by inverse CDF, against the definition in rational
+    arithmetic: seeded rows mixing ordinary, tiny (2^-100) and subnormal
+    float32 weights and exact zeros; plus a hand case where running sums in
+    float64 would pick another token: w = (.5, 2^-100, .5), u = .5 ->
+    u * total = .5 + 2^-101, so the tiny weight's token 1 is the answer
+    (float64 sums lose the 2^-100 and give 2)."""
+    if fn_icdf(np.array([.5, 2.0 ** -100, .5], dtype=np.float32), np.float32(.5)) != 1:
+        return False
+    rng = np.random.default_rng(seed)
+    for _ in range(200):
+        V = int(rng.integers(1, 24))
+        w = rng.random(V).astype(np.float32)
+        kind = rng.integers(0, 4, size=V)
+        w[kind == 1] = np.float32(2.0 ** -100) * (1 + np.float32(rng.random()))
+        w[kind == 2] = np.float32(1e-42)                          # subnormal
+        w[kind == 3] = 0
+        u = np.float32(rng.random())
+        if rng.random() < 0.2:                                   # u that lands on a boundary
+            tot = sum(float(x) for x in w)
+            u = np.float32(float(w[0]) / tot) if tot > 0 else u
+        want = _inverse_cdf_fractions(w, u)
+        if fn_icdf(w, u) != want:
+            return False
+    return True

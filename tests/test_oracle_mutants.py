@@ -184,6 +184,15 @@ def test_embedcat_mutant_harness_is_faithful():
 def _verify_mutant(slip):
     import oracle.verify64 as v
 
+    def icdf(w, u):
+        if slip == "float64_cdf":
+            w = np.asarray(w, dtype=np.float32)
+            if not (0 <= float(u) < 1) or not np.all((w >= 0) & (w <= 1)) or not np.any(w > 0):
+                return -1
+            c = np.cumsum(w.astype(np.float64))
+            return int(np.searchsorted(c, float(u) * c[-1], side="right"))
+        return v.inverse_cdf(w, u)
+
     def fn(p, q, draft, u_acc, u_res):
         p = np.asarray(p, dtype=np.float32)
         q = np.asarray(q, dtype=np.float32)
@@ -193,9 +202,17 @@ def _verify_mutant(slip):
         for b in range(B):
             j, rejected = N, False
             for i in range(N):
-                pd, qd = p[b, i, draft[b, i]], q[b, i, draft[b, i]]
-                ratio = pd / qd if slip == "inverted_ratio" else qd / pd
-                if not (pd <= 0 or u_acc[b, i] < min(np.float32(1), np.float32(ratio))):
+                t = int(draft[b, i])
+                inside = 0 <= t < V or slip == "wrap_ids"
+                pd = p[b, i, t % V] if inside else np.float32(0)
+                qd = q[b, i, t % V] if inside else np.float32(0)
+                if slip == "inverted_ratio":
+                    keep = np.float32(u_acc[b, i]) * qd < pd
+                elif slip == "keep_zero_p":
+                    keep = pd <= 0 or np.float32(u_acc[b, i]) * pd < qd
+                else:
+                    keep = np.float32(u_acc[b, i]) * pd < qd
+                if not keep:
                     if not rejected:
                         j, rejected = i, True
                     if slip != "no_stop":
@@ -210,21 +227,29 @@ def _verify_mutant(slip):
                     w = np.abs(q[b, j] - p[b, j])
                 else:
                     w = np.maximum(q[b, j] - p[b, j], 0)
-                if not np.any(w > 0):
+                if np.all((w >= 0) & (w <= 1)) and not np.any(w > 0):
                     w = q[b, j]
             else:
                 w = q[b, N - 1 if slip == "bonus_row" else N]
-            nxt[b] = v.inverse_cdf(w, u_res[b])
+            nxt[b] = icdf(w, u_res[b])
         return n_acc, nxt
-    return fn
+    return fn, icdf
 
 
-@pytest.mark.parametrize("slip", ["inverted_ratio", "flipped_residual", "unclipped", "bonus_row", "no_stop"])
+VERIFY_SLIPS = ["inverted_ratio", "flipped_residual", "unclipped", "bonus_row", "no_stop", "keep_zero_p",
+                "wrap_ids", "float64_cdf"]
+
+
+def _verify_pins_pass(fn, icdf):
+    return (pins.check_verify_hand(fn) and pins.check_verify_q_equals_p(fn) and pins.check_verify_leviathan(fn)
+            and pins.check_verify_zero_probability_drafts(fn) and pins.check_verify_invalid_rows(fn)
+            and pins.check_inverse_cdf_exact(icdf))
+
+
+@pytest.mark.parametrize("slip", VERIFY_SLIPS)
 def test_verify_mutants_fail_a_pin(slip):
-    fn = _verify_mutant(slip)
-    assert not (pins.check_verify_hand(fn) and pins.check_verify_q_equals_p(fn) and pins.check_verify_leviathan(fn))
+    assert not _verify_pins_pass(*_verify_mutant(slip))
 
 
 def test_verify_mutant_harness_is_faithful():
-    fn = _verify_mutant(None)
-    assert pins.check_verify_hand(fn) and pins.check_verify_q_equals_p(fn) and pins.check_verify_leviathan(fn)
+    assert _verify_pins_pass(*_verify_mutant(None))

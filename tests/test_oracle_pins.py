@@ -171,3 +171,18 @@ def test_verify_q_equals_p_keeps_everything():
 def test_verify_emitted_token_follows_q():
     import oracle.verify64 as v
     assert pins.check_verify_leviathan(v.verify_accept)
+
+
+def test_verify_zero_probability_drafts():
+    import oracle.verify64 as v
+    assert pins.check_verify_zero_probability_drafts(v.verify_accept)
+
+
+def test_verify_invalid_rows_give_no_token():
+    import oracle.verify64 as v
+    assert pins.check_verify_invalid_rows(v.verify_accept)
+
+
+def test_inverse_cdf_exact_against_fractions():
+    import oracle.verify64 as v
+    assert pins.check_inverse_cdf_exact(v.inverse_cdf)
