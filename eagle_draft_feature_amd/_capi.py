@@ -62,6 +62,7 @@ SIGNATURES = {
     "eagle31_last_hip_error": (_int, []),
     "eagle31_release": (_int, []),
     "eagle31_debug_stats_recompute": (_int, [_int]),
+    "eagle31_debug_fail_workspace_zero": (_int, [_int]),
 }
 
 

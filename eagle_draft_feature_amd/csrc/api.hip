@@ -2,8 +2,9 @@
 //
 // Every argument check runs on the host before the first HIP call; a failed
 // check enqueues nothing.  Dispatch: M <= 64 runs a single-launch decode
-// kernel, on W in its stored layout or on the folded weight tiles (both
-// split-K, statistics inside the launch); larger M runs the row-statistics pass and the folded GEMM,
+// kernel, on W in its stored layout or on the folded weight tiles (split-K,
+// statistics inside the launch; one token on the folded tiles: the whole-K
+// kernel).  Larger M runs the row-statistics pass and the folded GEMM,
 // preparing W', u and c into the workspace first when the caller passed the
 // stored W.
 #include <atomic>
@@ -137,6 +138,9 @@ struct OwnedWs {
 };
 
 std::mutex g_ws_mutex;
+// Test hook (eagle31_debug_fail_workspace_zero): the counter zeroing of a new
+// library-owned workspace reports a launch failure instead of running.
+std::atomic<int> g_zero_hook{0};
 std::map<std::pair<int, void*>, OwnedWs> g_ws;
 
 int owned_workspace(size_t need, hipStream_t st, void** out_ptr, size_t* out_bytes) {
@@ -156,14 +160,19 @@ int owned_workspace(size_t need, hipStream_t st, void** out_ptr, size_t* out_byt
         }
         size_t grow = need + need / 4;
         grow = up256(grow);
-        e = hipMalloc(&w.ptr, grow);
+        void* fresh = nullptr;
+        e = hipMalloc(&fresh, grow);
+        if (e != hipSuccess) return hip_fail(e);
+        // the buffer is kept only once its counters are zeroed: a buffer whose
+        // zeroing failed to launch is freed, so no later call can find it
+        e = g_zero_hook ? hipErrorLaunchFailure : launch_zero(fresh, COUNTER_REGION, st);
         if (e != hipSuccess) {
-            w.ptr = nullptr;
+            (void)hipStreamSynchronize(st);
+            (void)hipFree(fresh);
             return hip_fail(e);
         }
+        w.ptr = fresh;
         w.bytes = grow;
-        e = launch_zero(w.ptr, COUNTER_REGION, st);
-        if (e != hipSuccess) return hip_fail(e);
     }
     *out_ptr = w.ptr;
     *out_bytes = w.bytes;
@@ -354,6 +363,11 @@ size_t eagle31_workspace_size(int64_t M, int64_t d, int norm_kind) {
     const WsLayout a = layout_for(M, d, norm_kind, false);
     const WsLayout b = layout_for(M, d, norm_kind, true);
     return a.total > b.total ? a.total : b.total;
+}
+
+int eagle31_debug_fail_workspace_zero(int on) {
+    g_zero_hook.store(on ? 1 : 0, std::memory_order_relaxed);
+    return EAGLE31_OK;
 }
 
 int eagle31_debug_stats_recompute(int on) {

@@ -229,3 +229,9 @@ def debug_stats_recompute(on: bool) -> None:
     """Test hook: the folded decode kernel's statistics readers recompute the
     rows instead of waiting for the published records (same result)."""
     check("eagle31_debug_stats_recompute", lib().eagle31_debug_stats_recompute(1 if on else 0))
+
+
+def debug_fail_workspace_zero(on: bool) -> None:
+    """Test hook: the counter zeroing of a new library-owned workspace reports
+    a launch failure (and the buffer is not kept)."""
+    check("eagle31_debug_fail_workspace_zero", lib().eagle31_debug_fail_workspace_zero(1 if on else 0))

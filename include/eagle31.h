@@ -231,6 +231,16 @@ int eagle31_release(void);
  */
 int eagle31_debug_stats_recompute(int on);
 
+/*
+ * eagle31_debug_fail_workspace_zero - test hook: while on != 0, the zeroing of
+ * the counters of a newly allocated library-owned workspace reports a launch
+ * failure (the call returns EAGLE31_ERR_HIP) instead of running, and the new
+ * buffer is freed, so that a later call never finds a buffer whose counters
+ * were not zeroed.  Process-wide; always returns EAGLE31_OK.  Never needed in
+ * production.
+ */
+int eagle31_debug_fail_workspace_zero(int on);
+
 #ifdef __cplusplus
 }
 #endif

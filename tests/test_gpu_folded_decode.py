@@ -1,0 +1,134 @@
+"""The folded decode path (eagle31_fuse_folded, 2 <= M <= 64) against the
+fp64 oracle through the C ABI, at every token-tile count and at widths that
+change the split-K kernel's plan (columns per workgroup, waves, chunks per
+state, ring depth), for all three norms; the decode-shaped workloads at every
+token count; a 100-sigma DC offset through the fold; bitwise repeatability over
+many calls at alternating token counts; the workspace-zeroing failure hook.
+
+Tolerance: tests/parity.py (row-RMS-normalised max 2e-2, mean 4e-3).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import DevInputs, assert_parity, bf16_to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+LN, RMS, NONE = 1, 2, 0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import eagle_draft_feature_amd  # noqa: F401
+    yield
+    torch.cuda.synchronize()
+
+
+def e31():
+    import eagle_draft_feature_amd as m
+    return m
+
+
+def note(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def oracle_out(inp, kind, eps):
+    H = [oracle.decode_bf16(h) for h in inp.h]
+    g = [oracle.decode_bf16(x) for x in inp.gamma]
+    b = None if inp.beta is None else [oracle.decode_bf16(x) for x in inp.beta]
+    bias = None if inp.bias is None else oracle.decode_bf16(inp.bias)
+    return oracle.fuse(H, kind, eps, g, b, oracle.decode_bf16(inp.W), bias)
+
+
+def folded_call(dv, kind, eps, prepared=None):
+    wf, u, c = prepared if prepared is not None else e31().fold_prepare(kind, dv.gamma, dv.beta, dv.W, dv.bias)
+    out = e31().fuse_folded(dv.h[0], dv.h[1], dv.h[2], kind, eps, wf, u, c)
+    torch.cuda.synchronize()
+    return out, (wf, u, c)
+
+
+@pytest.mark.parametrize("d", [2048, 2560, 3072, 3584, 4096, 4608, 5120])
+@pytest.mark.parametrize("M", [2, 3, 16, 17, 33, 64])
+def test_folded_decode_parity(d, M):
+    kind = (LN, RMS, NONE)[(d // 512 + M) % 3]
+    eps = {LN: 1e-5, RMS: 1e-6, NONE: 0.0}[kind]
+    note(f"folded decode d={d} M={M} kind={kind}")
+    w = synth.gen.custom_workload(d, (M,), seed_tag=d * 13 + M)
+    inp = synth.make_inputs(w, M)
+    dv = DevInputs(inp)
+    out, _ = folded_call(dv, kind, eps)
+    assert_parity(bf16_to_f64(out), oracle_out(inp, kind, eps), f"folded d={d} M={M} kind={kind}")
+
+
+@pytest.mark.parametrize("kind", [LN, RMS, NONE])
+def test_folded_decode_every_norm_at_the_headline_shape(kind):
+    note(f"folded decode d=4096 M=64 kind={kind}")
+    inp = synth.make_inputs(2, 64)
+    dv = DevInputs(inp)
+    eps = {LN: 1e-5, RMS: 1e-6, NONE: 0.0}[kind]
+    out, _ = folded_call(dv, kind, eps)
+    assert_parity(bf16_to_f64(out), oracle_out(inp, kind, eps), f"folded headline kind={kind}")
+
+
+def test_folded_decode_bitwise_over_many_calls():
+    """Fifty calls back to back on one stream, at two token counts in turn:
+    every output is bit-identical to the first of its size."""
+    note("folded decode 50 repeats")
+    inp = synth.make_inputs(2, 64)
+    dv = DevInputs(inp)
+    prepared = e31().fold_prepare(LN, dv.gamma, dv.beta, dv.W, dv.bias)
+    refs = {}
+    for M in (64, 9):
+        h = [x[:M] for x in dv.h]
+        refs[M] = e31().fuse_folded(h[0], h[1], h[2], LN, 1e-5, *prepared)
+    outs = []
+    for i in range(50):
+        M = 64 if i % 2 == 0 else 9
+        h = [x[:M] for x in dv.h]
+        outs.append((M, e31().fuse_folded(h[0], h[1], h[2], LN, 1e-5, *prepared)))
+    torch.cuda.synchronize()
+    for M, o in outs:
+        assert torch.equal(o.view(torch.int16), refs[M].view(torch.int16)), f"repeat differs at M={M}"
+    assert_parity(bf16_to_f64(refs[9]), oracle_out(inp.rows(9), LN, 1e-5), "folded M=9")
+
+
+@pytest.mark.parametrize("M", [4, 64])
+def test_folded_decode_dc_offset(M):
+    """A shared offset of 100 sigma on h_high through the folded path: the
+    statistics' shifted sums and the fold's h.W' - mu.u cancellation hold."""
+    note(f"folded decode dc offset M={M}")
+    w = synth.gen.custom_workload(4096, (M,), seed_tag=71)
+    inp = synth.make_inputs(w, M, extra_offset=(0.0, 0.0, 1600.0))
+    dv = DevInputs(inp)
+    out, _ = folded_call(dv, LN, 1e-5)
+    assert_parity(bf16_to_f64(out), oracle_out(inp, LN, 1e-5), f"folded dc offset M={M}")
+
+
+def test_workspace_zeroing_failure_keeps_no_buffer():
+    """A library-owned workspace whose counter zeroing fails (forced by the
+    test hook) is not kept: the call reports the HIP failure, and the next
+    call on that stream allocates and zeroes a fresh buffer and is correct."""
+    note("workspace zero hook")
+    inp = synth.make_inputs(2, 64)
+    dv = DevInputs(inp)
+    prepared = e31().fold_prepare(LN, dv.gamma, dv.beta, dv.W, dv.bias)
+    s = torch.cuda.Stream()
+    e31().debug_fail_workspace_zero(True)
+    try:
+        with torch.cuda.stream(s):
+            with pytest.raises(e31().Eagle31Error):
+                e31().fuse_folded(dv.h[0], dv.h[1], dv.h[2], LN, 1e-5, *prepared)
+    finally:
+        e31().debug_fail_workspace_zero(False)
+    with torch.cuda.stream(s):
+        out = e31().fuse_folded(dv.h[0], dv.h[1], dv.h[2], LN, 1e-5, *prepared)
+    torch.cuda.synchronize()
+    assert_parity(bf16_to_f64(out), oracle_out(inp, LN, 1e-5), "after zero hook")

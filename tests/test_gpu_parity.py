@@ -2,9 +2,9 @@
 bfloat16 inputs.  Needs an MI355X: every test here is marked gpu.
 
 Tolerance: tests/parity.py (row-RMS-normalised max 2e-2, mean 4e-3).
-Full-size workloads whose oracle would take minutes are checked on sampled
-rows (first and last 8 plus a seeded sample), which the oracle computes one
-by one: the step is row independent.
+The full-size prefill workloads are checked on every row in
+tests/test_gpu_fullsize.py; the d=4160 pipeline-restart case here checks
+sampled rows plus its whole ragged last tile.
 """
 
 import numpy as np
@@ -114,28 +114,6 @@ def test_cfg3_tree_rmsnorm(M):
     assert_parity(G, oracle_rows(inp.rows(M), RMS, 1e-6), f"cfg3 M={M}")
 
 
-@pytest.mark.parametrize("M,kind,eps", [(512, LN, 1e-5), (512, RMS, 1e-6), (2048, LN, 1e-5), (4093, LN, 1e-5),
-                                        (4093, RMS, 1e-6), (4096, LN, 1e-5), (4096, RMS, 1e-6)])
-def test_cfg5_chunked_prefill(M, kind, eps):
-    note(f"cfg5 d=8192 M={M} kind={kind}")
-    inp = inputs(5, 4096)
-    dv = DevInputs(inp)
-    G = run_fuse(dv, kind, eps, M=M)
-    rows = sample_rows(M, 40, seed=M)
-    assert_parity(G[rows], oracle_rows(inp, kind, eps, rows=rows), f"cfg5 M={M} kind={kind}")
-
-
-def test_cfg4_long_prefill_sampled():
-    note("cfg4 d=7168 M=32768 LN (sampled rows)")
-    inp = synth.make_inputs(4)
-    dv = DevInputs(inp)
-    G = run_fuse(dv, LN, 1e-5)
-    rows = sample_rows(inp.M, 48, seed=4)
-    assert_parity(G[rows], oracle_rows(inp, LN, 1e-5, rows=rows), "cfg4 sampled")
-    del dv
-    torch.cuda.empty_cache()
-
-
 @pytest.mark.parametrize("folded", [False, True])
 def test_prefill_state_restart_ragged(folded):
     """Prefill without split-K at a width whose state length is not a whole
@@ -180,9 +158,9 @@ def test_fold_prepare_exact_weight_and_vectors(cfg, kind, eps):
     assert np.max(np.abs(c.cpu().numpy() - co)) <= 1e-5 * max(np.abs(co).max(), 1e-3) + 1e-6
 
 
-@pytest.mark.parametrize("cfg,M,kind,eps", [(1, 64, LN, 1e-5), (2, 1, LN, 1e-5), (2, 64, LN, 1e-5),
-                                            (3, 64, RMS, 1e-6), (3, 256, RMS, 1e-6), (5, 4096, LN, 1e-5),
-                                            (5, 4093, RMS, 1e-6)])
+@pytest.mark.parametrize("cfg,M,kind,eps", [(1, 64, LN, 1e-5), (2, 1, LN, 1e-5), (2, 4, LN, 1e-5), (2, 8, LN, 1e-5),
+                                            (2, 16, LN, 1e-5), (2, 32, LN, 1e-5), (2, 64, LN, 1e-5),
+                                            (3, 64, RMS, 1e-6), (3, 128, RMS, 1e-6), (3, 256, RMS, 1e-6)])
 def test_fuse_folded_parity(cfg, M, kind, eps):
     note(f"fuse_folded cfg{cfg} M={M} kind={kind}")
     inp = inputs(cfg, synth.CONFIGS[cfg].max_M if cfg != 2 else 64)
@@ -192,9 +170,7 @@ def test_fuse_folded_parity(cfg, M, kind, eps):
     out = e31().fuse_folded(h[0], h[1], h[2], kind, eps, wf, u, c)
     torch.cuda.synchronize()
     G = bf16_to_f64(out)
-    rows = sample_rows(M, 40, seed=M + 1)
-    sub = inp.rows(M)
-    assert_parity(G[rows], oracle_rows(sub, kind, eps, rows=rows), f"folded cfg{cfg} M={M}")
+    assert_parity(G, oracle_rows(inp.rows(M), kind, eps), f"folded cfg{cfg} M={M}")
 
 
 @pytest.mark.parametrize("cfg,M,kind,eps", [(2, 1, LN, 1e-5), (2, 64, LN, 1e-5), (3, 64, RMS, 1e-6),
