@@ -25,6 +25,7 @@ ERR_ALIGN = -5
 ERR_HIP = -6
 ERR_WORKSPACE = -7
 ERR_ALIAS = -8
+ERR_TOO_LARGE = -9
 
 STATUS_NAMES = {
     OK: "EAGLE31_OK",
@@ -36,6 +37,7 @@ STATUS_NAMES = {
     ERR_HIP: "EAGLE31_ERR_HIP",
     ERR_WORKSPACE: "EAGLE31_ERR_WORKSPACE",
     ERR_ALIAS: "EAGLE31_ERR_ALIAS",
+    ERR_TOO_LARGE: "EAGLE31_ERR_TOO_LARGE",
 }
 
 # Every symbol the header declares, with (restype, argtypes).
@@ -55,6 +57,8 @@ SIGNATURES = {
     "eagle31_fuse_folded": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _f32, _vp, _vp, _vp, _vp, _vp]),
     "eagle31_fuse_folded_ws": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _f32, _vp, _vp, _vp, _vp, _vp, _sz,
                                       _vp]),
+    "eagle31_fuse_folded_noalloc": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _f32, _vp, _vp, _vp, _vp, _vp]),
+    "eagle31_noalloc_scratch_bytes": (_sz, []),
     "eagle31_row_stats": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _f32, _vp, _vp, _vp]),
     "eagle31_norm_output": (_int, [_vp, _i64, _i64, _int, _f32, _vp, _vp, _vp, _vp]),
     "eagle31_embed_concat": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),

@@ -179,6 +179,41 @@ int owned_workspace(size_t need, hipStream_t st, void** out_ptr, size_t* out_byt
     return EAGLE31_OK;
 }
 
+// ------------------------------------------- fixed scratch of the no-alloc entry
+// eagle31_fuse_folded_noalloc runs on this array instead of allocated
+// workspace.  Each device holds its own copy (for as long as the library is
+// loaded).  In host code its name is only a stand-in: the device address is
+// taken once per device with hipGetSymbolAddress, and only that address is
+// passed to kernels or zeroed.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+// The device address of the current device's scratch.  On the first call on
+// a device it is looked up and the counter region (which every call leaves at
+// zero) is zeroed by a kernel on `st`.
+int noalloc_scratch(hipStream_t st, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return hip_fail(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e);
+        if (p == nullptr || ((uintptr_t)p & 255u) != 0) return hip_fail(hipErrorInvalidSymbol);
+        e = launch_zero(p, COUNTER_REGION, st);
+        if (e != hipSuccess) return hip_fail(e);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return EAGLE31_OK;
+}
+
 // Id stamped on the statistics records of one decode call: process-wide,
 // never 0 (a zeroed workspace holds no valid record), so a record left by an
 // earlier call on the same workspace never matches.
@@ -450,6 +485,23 @@ int eagle31_fuse_folded_ws(const void* h_low, const void* h_mid, const void* h_h
                     true, out, workspace, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
+int eagle31_fuse_folded_noalloc(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d,
+                                int norm_kind, float eps, const void* w_folded, const float* u, const float* c,
+                                void* out, void* stream) {
+    int r = validate_folded(h_low, h_mid, h_high, M, d, norm_kind, eps, w_folded, u, c, out);
+    if (r != EAGLE31_OK || M == 0) return r;
+    const size_t need = layout_for(M, d, norm_kind, true).total;
+    if (need > NOALLOC_SCRATCH_BYTES) return EAGLE31_ERR_TOO_LARGE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    r = noalloc_scratch(st, &ws);
+    if (r != EAGLE31_OK) return r;
+    return run_fuse(h_low, h_mid, h_high, M, d, norm_kind, eps, nullptr, nullptr, nullptr, nullptr, w_folded, u, c,
+                    true, out, ws, NOALLOC_SCRATCH_BYTES, st);
+}
+
+size_t eagle31_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
 int eagle31_row_stats(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d, int norm_kind,
                       float eps, float* mu, float* rstd, void* stream) {
     int r = check_common(M, d, norm_kind, eps);
@@ -520,6 +572,7 @@ const char* eagle31_status_string(int status) {
         case EAGLE31_ERR_HIP: return "a HIP runtime call failed";
         case EAGLE31_ERR_WORKSPACE: return "workspace missing or too small";
         case EAGLE31_ERR_ALIAS: return "out overlaps an input";
+        case EAGLE31_ERR_TOO_LARGE: return "the problem needs more scratch than the no-alloc entry point's fixed array";
         default: return "unknown status";
     }
 }

@@ -166,6 +166,25 @@ def fuse_folded(h_low, h_mid, h_high, norm, eps, w_folded: torch.Tensor, u: torc
     return out
 
 
+def fuse_folded_noalloc(h_low, h_mid, h_high, norm, eps, w_folded: torch.Tensor, u: torch.Tensor, c: torch.Tensor,
+                        out: torch.Tensor) -> torch.Tensor:
+    """eagle31_fuse_folded_noalloc: the folded step on the library's fixed
+    scratch array.  `out` must be given: nothing is allocated here either."""
+    M, d, dev = _states(h_low, h_mid, h_high)
+    _want(w_folded, "w_folded", shape=folded_shape(d), device=dev)
+    _want(u, "u", dtype=torch.float32, shape=(3, d), device=dev)
+    _want(c, "c", dtype=torch.float32, shape=(d,), device=dev)
+    _want(out, "out", shape=(M, d), device=dev)
+    st = lib().eagle31_fuse_folded_noalloc(_ptr(h_low), _ptr(h_mid), _ptr(h_high), M, d, norm_kind(norm), float(eps),
+                                           _ptr(w_folded), _ptr(u), _ptr(c), _ptr(out), _stream(h_low))
+    check("eagle31_fuse_folded_noalloc", st)
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().eagle31_noalloc_scratch_bytes())
+
+
 def row_stats(h_low, h_mid, h_high, norm, eps):
     """eagle31_row_stats: returns (mu [3, M], rstd [3, M]) float32."""
     M, d, dev = _states(h_low, h_mid, h_high)

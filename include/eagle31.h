@@ -66,7 +66,8 @@ enum eagle31_status {
     EAGLE31_ERR_ALIGN = -5,      /* a pointer is not 16-byte aligned */
     EAGLE31_ERR_HIP = -6,        /* a HIP runtime call failed */
     EAGLE31_ERR_WORKSPACE = -7,  /* caller workspace NULL or too small */
-    EAGLE31_ERR_ALIAS = -8       /* out overlaps an input */
+    EAGLE31_ERR_ALIAS = -8,      /* out overlaps an input */
+    EAGLE31_ERR_TOO_LARGE = -9   /* needs more scratch than eagle31_fuse_folded_noalloc has */
 };
 
 /*
@@ -155,6 +156,30 @@ int eagle31_fuse_folded(const void* h_low, const void* h_mid, const void* h_high
 int eagle31_fuse_folded_ws(const void* h_low, const void* h_mid, const void* h_high, int64_t M,
                            int64_t d, int norm_kind, float eps, const void* w_folded, const float* u,
                            const float* c, void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * eagle31_fuse_folded_noalloc - eagle31_fuse_folded for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the scratch memory (split-K partials,
+ * statistics records, counters) is a fixed array inside the library, one per
+ * device, eagle31_noalloc_scratch_bytes() bytes (16 MiB), held until the
+ * process ends.  The call performs no allocation of its own; the caller still
+ * provides every input and output.  Arguments, result and errors are those of
+ * eagle31_fuse_folded, plus EAGLE31_ERR_TOO_LARGE (nothing enqueued) when the
+ * problem's scratch exceeds the array: every decode call (M <= 64) up to
+ * d = 8192 fits, and prefill calls whose tile count needs no split-K
+ * (e.g. d = 8192, M = 4096; d = 7168, M = 32768).
+ * The first call on a device also enqueues the zeroing of the array's
+ * counters on `stream`.  All calls on one device share its array and each
+ * leaves its counters at zero: calls that overlap in time on one device (two
+ * streams, two host threads) race and give undefined results; order them.
+ */
+int eagle31_fuse_folded_noalloc(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d,
+                                int norm_kind, float eps, const void* w_folded, const float* u, const float* c,
+                                void* out, void* stream);
+
+/* Bytes of the fixed scratch array behind eagle31_fuse_folded_noalloc. */
+size_t eagle31_noalloc_scratch_bytes(void);
 
 /*
  * eagle31_row_stats - the statistics pass on its own: per state s and token m,
