@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurements")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
     p.add_argument("--only", choices=["decode", "decode_folded", "prefill", "rowstats", "copy", "postnorm", "postnorm_decode",
-                                             "embedcat"], default=None,
+                                             "embedcat", "verify"], default=None,
                    help="run a single leg (used under rocprofv3)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
@@ -305,6 +305,50 @@ def embedcat_leg(torch, pkg, synth, M, d, steps, warmup, vocab=32000):
     return res
 
 
+def verify_leg(torch, pkg, synth, V, B=64, N=4, steps=100, warmup=10):
+    """eagle31_verify_accept on B sequences x N drafts over a V-token
+    vocabulary.  The step must read, per sequence, the rows it samples from:
+    q_j and p_j (2 V floats) after a rejection, q_N (V floats) when every
+    draft is kept; plus the draft positions' p and q values, the drafts and the
+    uniforms.  Those bytes over the call time give the HBM fraction.  Copies of
+    the inputs are rotated so the sampled rows are not cache-resident."""
+    import numpy as np
+    p, q, draft, u_acc, u_res = synth.make_verify_inputs(B, N, V, seed=V, spread=0.5)
+    per_set = (p.nbytes + q.nbytes)
+    n_o = None
+    sets = []
+    base = [torch.from_numpy(x).to("cuda") for x in (p, q, draft, u_acc, u_res)]
+    n_acc, nxt = pkg.verify_accept(*base)
+    torch.cuda.synchronize()
+    n_o = n_acc.cpu().numpy()
+    rows_read = int(np.sum(np.where(n_o < N, 2, 1)))
+    bytes_alg = rows_read * V * 4 + B * N * (4 + 4 + 4 + 4) + B * 4 + 2 * B * 4
+    R = max(2, -(-2 * MALL_BYTES // max(1, rows_read * V * 4)))
+    R = min(R, max(2, int(6e9 // per_set)))
+    for r in range(R):
+        sets.append(base if r == 0 else [x.clone() for x in base])
+    outs = [(torch.empty(B, dtype=torch.int32, device="cuda"), torch.empty(B, dtype=torch.int32, device="cuda"))
+            for _ in range(R)]
+
+    def fn(i):
+        s = sets[i]
+        pkg.verify_accept(*s, n_accepted=outs[i][0], next_token=outs[i][1])
+
+    times = []
+    for _ in range(5):
+        t, _ = time_loop(torch, fn, R, steps, warmup)
+        times.append(t / steps)
+    per = statistics.median(times)
+    res = dict(entry="eagle31_verify_accept", kernel="verify_kernel", B=B, N=N, V=V, R=R, steps=steps,
+               us_per_call=round(per * 1e6, 3), us_p10=round(sorted(times)[0] * 1e6, 3),
+               us_p90=round(sorted(times)[-1] * 1e6, 3), kept_mean=round(float(n_o.mean()), 3),
+               bytes_per_call=bytes_alg, gbs=round(bytes_alg / per / 1e9, 1),
+               hbm_frac=round(bytes_alg / per / 1e9 / HBM_PEAK_GBS, 4))
+    del sets, outs, base
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline_leg(inp, kind, eps, budget_s):
     """The fp64 oracle as it stands, on preconverted float64 arrays, repeated
     until about budget_s seconds of host work."""
@@ -371,6 +415,9 @@ def main():
         return
     if args.only == "prefill":
         print(json.dumps(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, max(3, args.steps), args.warmup, folded=True)))
+        return
+    if args.only == "verify":
+        print(json.dumps([verify_leg(torch, pkg, synth, V) for V in (32000, 128256, 151936)]))
         return
     if args.only == "embedcat":
         print(json.dumps([embedcat_leg(torch, pkg, synth, 64, 4096, max(50, args.steps), args.warmup),
@@ -456,6 +503,9 @@ def main():
     if not args.no_prefill:
         embedcat.append(embedcat_leg(torch, pkg, synth, 32768, 7168, 20, 5))
 
+    # the verify / accept step over the vocabulary (a next step of the path)
+    verify = [verify_leg(torch, pkg, synth, V) for V in (32000, 128256, 151936)]
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline_leg(dec["inp"], dec["kind"], dec["eps"], args.cpu_seconds)
@@ -485,6 +535,7 @@ def main():
         "other_workloads": others,
         "postnorm": postnorm,
         "embed_concat": embedcat,
+        "verify": verify,
     }
     print(json.dumps(line))
 

@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libeagle31.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "k_rowstats.hip", "k_decode.hip", "k_gemv.hip", "k_prefill.hip", "k_fold.hip", "k_normout.hip", "k_embedcat.hip"]
+SOURCES = ["api.hip", "k_rowstats.hip", "k_decode.hip", "k_gemv.hip", "k_prefill.hip", "k_fold.hip", "k_normout.hip", "k_embedcat.hip", "k_verify.hip"]
 
 # Packed FP32 instructions are kept out of the device code.
 HIPCC_FLAGS = [

@@ -44,6 +44,7 @@ bool overlaps(const void* p, size_t bytes, const void* q, size_t qbytes) {
 
 constexpr int64_t MAX_M = 16777216;
 constexpr int64_t MAX_D = 65536;
+constexpr int64_t VERIFY_MAX_V = 1 << 26;  // vocabulary size, at most
 
 int check_common(int64_t M, int64_t d, int norm_kind, float eps) {
     if (M < 0 || M > MAX_M || d <= 0 || d > MAX_D || (d % 64) != 0) return EAGLE31_ERR_SHAPE;
@@ -557,6 +558,55 @@ int eagle31_embed_concat(const int32_t* tokens, int64_t M, int64_t d, int64_t vo
     const hipError_t e = launch_embed_concat(tokens, (int)M, (int)d, (int)vocab, static_cast<const uint16_t*>(embed),
                                              static_cast<const uint16_t*>(fused), static_cast<uint16_t*>(dst),
                                              bad_count, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e);
+    return EAGLE31_OK;
+}
+
+int eagle31_verify_accept(const float* p, const float* q, const int32_t* draft, const float* u_acc,
+                          const float* u_res, int64_t B, int64_t N, int64_t V, int32_t* n_accepted,
+                          int32_t* next_token, void* stream) {
+    if (B < 0 || B > MAX_COUNTERS || N < 1 || N > VERIFY_MAX_N || V < 1 || V > VERIFY_MAX_V) return EAGLE31_ERR_SHAPE;
+    if (B == 0) return EAGLE31_OK;
+    if (p == nullptr || q == nullptr || draft == nullptr || u_acc == nullptr || u_res == nullptr ||
+        n_accepted == nullptr || next_token == nullptr)
+        return EAGLE31_ERR_NULL;
+    const void* in4[5] = {p, q, draft, u_acc, u_res};
+    for (const void* x : in4)
+        if (((uintptr_t)x & 3u) != 0) return EAGLE31_ERR_ALIGN;
+    if (((uintptr_t)n_accepted & 3u) != 0 || ((uintptr_t)next_token & 3u) != 0) return EAGLE31_ERR_ALIGN;
+    const size_t pb = (size_t)B * N * V * 4, qb = (size_t)B * (N + 1) * V * 4, nb = (size_t)B * N * 4,
+                 ob = (size_t)B * 4;
+    const void* outs[2] = {n_accepted, next_token};
+    for (const void* o : outs)
+        if (overlaps(o, ob, p, pb) || overlaps(o, ob, q, qb) || overlaps(o, ob, draft, nb) ||
+            overlaps(o, ob, u_acc, nb) || overlaps(o, ob, u_res, ob))
+            return EAGLE31_ERR_ALIAS;
+    if (overlaps(n_accepted, ob, next_token, ob)) return EAGLE31_ERR_ALIAS;
+    const VerifyPlan plan = plan_verify((int)B, (int)N, (int)V);
+    if (!plan.ok) return EAGLE31_ERR_SHAPE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    void* ws = nullptr;
+    size_t wsb = 0;
+    const int r = owned_workspace(COUNTER_REGION + up256(plan.rec_bytes), st, &ws, &wsb);
+    if (r != EAGLE31_OK) return r;
+    VerifyArgs a;
+    a.p = p;
+    a.q = q;
+    a.draft = draft;
+    a.u_acc = u_acc;
+    a.u_res = u_res;
+    a.B = (int)B;
+    a.N = (int)N;
+    a.V = (int)V;
+    a.C = plan.C;
+    a.L = plan.L;
+    a.n_acc = n_accepted;
+    a.next = next_token;
+    a.counters = at<int>(ws, 0);
+    a.rec = at<uint64_t>(ws, COUNTER_REGION);
+    const bool vec = (V % 4) == 0 && ((uintptr_t)p & 15u) == 0 && ((uintptr_t)q & 15u) == 0;
+    const hipError_t e = launch_verify(a, plan, vec, st);
     if (e != hipSuccess) return hip_fail(e);
     return EAGLE31_OK;
 }

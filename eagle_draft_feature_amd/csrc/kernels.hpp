@@ -125,6 +125,28 @@ struct PrefillPlan {
 PrefillPlan plan_prefill(int M, int d);
 hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& p, hipStream_t st);
 
+// ------------------------------------------------------------ verify / accept
+constexpr int VERIFY_MAX_N = 64;  // drafts per sequence (one wave decides them)
+struct VerifyArgs {
+    const float* p;        // [B, N, V]
+    const float* q;        // [B, N + 1, V]
+    const int32_t* draft;  // [B, N]
+    const float* u_acc;    // [B, N]
+    const float* u_res;    // [B]
+    int B, N, V;
+    int C, L;              // chunks per sequence, tokens per chunk (from the plan)
+    int32_t* n_acc;        // [B]
+    int32_t* next;         // [B]
+    int* counters;         // [B], zero on entry, left zero
+    uint64_t* rec;         // [B][C][8]: exact digit sums and flags of each chunk
+};
+struct VerifyPlan {
+    int ok = 0, C = 0, L = 0;
+    size_t rec_bytes = 0;
+};
+VerifyPlan plan_verify(int B, int N, int V);
+hipError_t launch_verify(const VerifyArgs& a, const VerifyPlan& p, bool vec, hipStream_t st);
+
 // zero-fill helper (a kernel, not hipMemsetAsync)
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t st);
 

@@ -240,6 +240,31 @@ def embed_concat(tokens, embed, fused, out=None, bad_count=None):
     return out
 
 
+def verify_accept(p: torch.Tensor, q: torch.Tensor, draft: torch.Tensor, u_acc: torch.Tensor, u_res: torch.Tensor,
+                  n_accepted: Optional[torch.Tensor] = None, next_token: Optional[torch.Tensor] = None):
+    """eagle31_verify_accept: p [B, N, V], q [B, N+1, V] float32, draft [B, N]
+    int32, u_acc [B, N], u_res [B] float32 -> (n_accepted [B], next_token [B]) int32."""
+    if p.dim() != 3:
+        raise ValueError("p must be [B, N, V]")
+    B, N, V = p.shape
+    dev = p.device
+    _want(p, "p", dtype=torch.float32, device=dev)
+    _want(q, "q", dtype=torch.float32, shape=(B, N + 1, V), device=dev)
+    _want(draft, "draft", dtype=torch.int32, shape=(B, N), device=dev)
+    _want(u_acc, "u_acc", dtype=torch.float32, shape=(B, N), device=dev)
+    _want(u_res, "u_res", dtype=torch.float32, shape=(B,), device=dev)
+    if n_accepted is None:
+        n_accepted = torch.empty(B, dtype=torch.int32, device=dev)
+    if next_token is None:
+        next_token = torch.empty(B, dtype=torch.int32, device=dev)
+    _want(n_accepted, "n_accepted", dtype=torch.int32, shape=(B,), device=dev)
+    _want(next_token, "next_token", dtype=torch.int32, shape=(B,), device=dev)
+    st = lib().eagle31_verify_accept(_ptr(p), _ptr(q), _ptr(draft), _ptr(u_acc), _ptr(u_res), B, N, V,
+                                     _ptr(n_accepted), _ptr(next_token), _stream(p))
+    check("eagle31_verify_accept", st)
+    return n_accepted, next_token
+
+
 def release() -> None:
     check("eagle31_release", lib().eagle31_release())
 

@@ -232,6 +232,40 @@ int eagle31_norm_output(const void* x, int64_t M, int64_t d, int norm_kind, floa
 int eagle31_embed_concat(const int32_t* tokens, int64_t M, int64_t d, int64_t vocab, const void* embed,
                          const void* fused, void* dst, int32_t* bad_count, void* stream);
 
+/*
+ * eagle31_verify_accept - the speculative-decoding verify / accept step for a
+ * batch of B sequences with N drafts each (the Leviathan rule of the
+ * speculative-decoding lesson, factory.pai-world.com/.../15-speculative-decoding-eagle3,
+ * section "불변식: Leviathan 거부 샘플링"):
+ *
+ *   the drafts are taken left to right; draft d = draft[b][i] is kept iff
+ *       u_acc[b][i] * p[b][i][d] < q[b][i][d]   (the product rounded to float32:
+ *   the keep probability min(1, q/p) without a division; a draft with p = 0 is
+ *   kept iff q > 0; an id outside [0, V) is rejected);
+ *   at the first rejection j the next token is drawn from the residual
+ *   w = max(q[b][j] - p[b][j], 0) (float32 difference), or from q[b][j] when
+ *   every residual weight is zero; when all N are kept, from q[b][N];
+ *   the draw is the inverse CDF in token order in exact arithmetic: the
+ *   smallest t with w_0 + ... + w_t > u_res[b] * (w_0 + ... + w_{V-1}).
+ *
+ * p:          float32 [B, N, V], the drafter's distribution at each draft position;
+ * q:          float32 [B, N + 1, V], the verifier's;
+ * draft:      int32 [B, N]; u_acc: float32 [B, N]; u_res: float32 [B] (uniforms in
+ *             [0, 1), supplied by the caller);
+ * n_accepted: int32 [B], the drafts kept (j);
+ * next_token: int32 [B], the token emitted after them, or -1 when the weights it
+ *             is drawn from are all zero, hold NaN or a value above 1, or
+ *             u_res is outside [0, 1).
+ * All device memory, row-major, 4-byte aligned; outputs must not overlap
+ * inputs.  Limits: 0 <= B <= 4096, 1 <= N <= 64, 1 <= V <= 2^26
+ * (EAGLE31_ERR_SHAPE).  B == 0 launches nothing.  Uses library-owned scratch
+ * memory (per device and stream, as eagle31_fuse).  Deterministic: the result
+ * is unique (exact arithmetic), whatever the order of summation.
+ */
+int eagle31_verify_accept(const float* p, const float* q, const int32_t* draft, const float* u_acc,
+                          const float* u_res, int64_t B, int64_t N, int64_t V, int32_t* n_accepted,
+                          int32_t* next_token, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* eagle31_status_string(int status);
 

@@ -9,6 +9,7 @@ computation.
 
 from .workloads import CONFIGS, Workload, workload
 from .gen import Inputs, make_inputs, make_embed_inputs, bf16_round, bf16_bits, bits_to_f32
+from .verify import make_verify_inputs
 
 __all__ = [
     "CONFIGS",
@@ -17,6 +18,7 @@ __all__ = [
     "Inputs",
     "make_inputs",
     "make_embed_inputs",
+    "make_verify_inputs",
     "bf16_round",
     "bf16_bits",
     "bits_to_f32",
