@@ -63,6 +63,7 @@ SIGNATURES = {
     "eagle31_norm_output": (_int, [_vp, _i64, _i64, _int, _f32, _vp, _vp, _vp, _vp]),
     "eagle31_embed_concat": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "eagle31_verify_accept": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "eagle31_verify_chunking": (_int, [_i64, _i64, _i64, _vp, _vp]),
     "eagle31_status_string": (ctypes.c_char_p, [_int]),
     "eagle31_last_hip_error": (_int, []),
     "eagle31_release": (_int, []),

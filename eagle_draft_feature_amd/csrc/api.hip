@@ -611,6 +611,16 @@ int eagle31_verify_accept(const float* p, const float* q, const int32_t* draft, 
     return EAGLE31_OK;
 }
 
+int eagle31_verify_chunking(int64_t B, int64_t N, int64_t V, int32_t* chunks, int32_t* tokens_per_chunk) {
+    if (B < 1 || B > MAX_COUNTERS || N < 1 || N > VERIFY_MAX_N || V < 1 || V > VERIFY_MAX_V) return EAGLE31_ERR_SHAPE;
+    if (chunks == nullptr || tokens_per_chunk == nullptr) return EAGLE31_ERR_NULL;
+    const VerifyPlan plan = plan_verify((int)B, (int)N, (int)V);
+    if (!plan.ok) return EAGLE31_ERR_SHAPE;
+    *chunks = plan.C;
+    *tokens_per_chunk = plan.L;
+    return EAGLE31_OK;
+}
+
 const char* eagle31_status_string(int status) {
     switch (status) {
         case EAGLE31_OK: return "ok";

@@ -17,21 +17,22 @@
 // integer prefix S_t, S_t > u_res T <=> S_t > floor(u_res T).
 //
 // Work split (HBM-bound: the sampled row or row pair is read once).  A
-// sequence's row is cut into C chunks of L tokens, one workgroup each
-// (B * C workgroups, chunks of 8192 tokens or more, at most 256 per row).
-// Every workgroup finds j itself (N loads), sums its chunk's weights exactly
-// (all of a thread's loads issued before the first is used; per lane into
-// four exponent bands of 64-bit sums, one add per token, turned into digits
-// at the end), flags invalid values (NaN, above 1)
-// and positive ones, and publishes the record; the last workgroup of the
-// sequence to arrive (device-scope counter) loads every record at once (one
-// per thread), scans them to get the total and each chunk's prefix, forms the
-// threshold, picks the first chunk whose prefix exceeds it, and searches that
-// chunk: each wave loads its quarter into registers and sums it, then the
-// wave whose quarter holds the crossing scans its registers 256 tokens at a
-// time with a lane-level inclusive scan of digit sums.  A
-// residual that is all zero (only when q_j <= p_j everywhere) makes the last
-// arriver sum and search q_j over the whole row itself.
+// sequence's row is cut into C chunks of L tokens (2048, 4096 or 8192: small
+// batches take small chunks so that more CUs share a row; at most 256 chunks
+// per row), one workgroup each, and each chunk into four quarters, one per
+// wave.  Every workgroup finds j itself (N loads); each wave sums its
+// quarter's weights exactly (a lane issues all its loads of a 2048-token
+// block before using any; per lane into four exponent bands of 64-bit sums,
+// one add per token, turned into digits at the end), flags invalid values
+// (NaN, above 1) and positive ones, and publishes its quarter record; the
+// last workgroup of the sequence to arrive (device-scope counter) loads
+// every chunk's record at once (one chunk per thread), scans the chunk totals
+// to get the total and each chunk's prefix, forms the threshold, picks the
+// first chunk whose prefix exceeds it and, from that chunk's quarter sums, the
+// quarter.  Only that quarter is read again: 8 tokens per thread, one load
+// round, a workgroup scan of the thread sums, then the chosen thread walks
+// its tokens.  A residual that is all zero (only when q_j <= p_j everywhere)
+// makes the last arriver sum and search q_j over the whole row itself.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -282,9 +283,8 @@ __device__ void wg_range_sum(const WRow& r, int a, int len, Dig& sum, uint32_t& 
     __syncthreads();
 }
 
-constexpr int VF_L = 8192;                    // tokens per chunk (rows up to 256 chunks)
-constexpr int VF_SPT = VF_L / (4 * VF_THREADS);  // float4 steps per thread in a chunk
-constexpr int VF_QS = VF_L / 4 / 256;          // 256-token steps in a quarter chunk
+constexpr int VF_QMAX = 2048;  // tokens in a block of the quarter sum (32 per lane); longest fast-searched quarter
+constexpr int VF_REC = 24;     // u64 words of a chunk record: four quarter digit sums, four flag words
 
 // weights of 4 consecutive tokens from loaded q (and p) vectors
 __device__ __forceinline__ void w4(const WRow& r, const f32x4& qv, const f32x4& pv, float (&w)[4], uint32_t& bad,
@@ -307,49 +307,69 @@ __device__ __forceinline__ void w4(const WRow& r, const f32x4& qv, const f32x4& 
     }
 }
 
-// Exact sum of a whole chunk [a, a + VF_L) of aligned rows: each thread's
-// VF_SPT vector loads (of q and p) are issued before any is used.
-__device__ void wg_chunk_sum(const WRow& r, int a, Dig& sum, uint32_t& bad, uint32_t& pos, Dig* sh_dig,
-                             uint32_t* sh_flag) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    f32x4 qv[VF_SPT], pv[VF_SPT];
-#pragma unroll
-    for (int k = 0; k < VF_SPT; ++k) {
-        const int i = a + 4 * tid + 4 * VF_THREADS * k;
-        qv[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r.q + i));
-        pv[k] = r.mode == 0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r.p + i)) : qv[k];
-    }
-    Band band;
-    band_zero(band);
-    uint32_t b = 0, ps = 0;
-#pragma unroll
-    for (int k = 0; k < VF_SPT; ++k) {
-        float w[4];
-        w4(r, qv[k], pv[k], w, b, ps);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) band_add_w(band, w[e]);
-    }
-    Dig acc;
+// Exact sum of the weights [qa, qa + qlen) by one wave (every lane gets it);
+// bad / pos OR-ed per lane, not across the wave.  Blocks of 2048 tokens: a
+// lane issues all its loads of a block (8 vectors of q and of p, or 32
+// scalars each when rows are not 16-byte aligned) before using any.  With VEC
+// the range ends on a multiple of 4 tokens.
+template <bool VEC>
+__device__ void wave_range_sum(const WRow& r, int qa, int qlen, Dig& acc, uint32_t& bad, uint32_t& pos) {
+    const int lane = threadIdx.x & 63;
+    const int qe = qa + qlen;
     dig_zero(acc);
-    band_flush(band, acc);
-    acc = dig_wave_sum(acc);
-    b = __any(b) ? 1u : 0u;
-    ps = __any(ps) ? 1u : 0u;
-    if (lane == 0) {
-        sh_dig[wave] = acc;
-        sh_flag[wave] = b | (ps << 1);
-    }
-    __syncthreads();
-    dig_zero(sum);
-    uint32_t f = 0;
+    for (int i0 = qa; i0 < qe; i0 += VF_QMAX) {
+        Band band;
+        band_zero(band);
+        if (VEC) {
+            f32x4 qv[8], pv[8];
+            const f32x4* qb = reinterpret_cast<const f32x4*>(r.q + i0) + lane;
+            const f32x4* pb = reinterpret_cast<const f32x4*>(r.p + i0) + lane;
+            if (i0 + VF_QMAX <= qe) {  // a whole block
 #pragma unroll
-    for (int w = 0; w < VF_THREADS / 64; ++w) {
-        dig_add(sum, sh_dig[w]);
-        f |= sh_flag[w];
+                for (int k = 0; k < 8; ++k) qv[k] = __builtin_nontemporal_load(qb + 64 * k);
+                if (r.mode == 0) {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) pv[k] = __builtin_nontemporal_load(pb + 64 * k);
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) pv[k] = qv[k];
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const bool in = i0 + 4 * lane + 256 * k < qe;
+                    qv[k] = in ? __builtin_nontemporal_load(qb + 64 * k) : f32x4{0, 0, 0, 0};
+                    pv[k] = in && r.mode == 0 ? __builtin_nontemporal_load(pb + 64 * k) : qv[k];
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                float w[4];
+                w4(r, qv[k], pv[k], w, bad, pos);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) band_add_w(band, w[e]);
+            }
+        } else {
+            float qs[32], ps[32];
+#pragma unroll
+            for (int k = 0; k < 32; ++k) {
+                const int i = i0 + lane + 64 * k;
+                const bool in = i < qe;
+                qs[k] = in ? r.q[i] : 0.0f;
+                ps[k] = in && r.mode == 0 ? r.p[i] : qs[k];
+            }
+#pragma unroll
+            for (int k = 0; k < 32; k += 4) {
+                float w[4];
+                w4(r, f32x4{qs[k], qs[k + 1], qs[k + 2], qs[k + 3]}, f32x4{ps[k], ps[k + 1], ps[k + 2], ps[k + 3]}, w,
+                   bad, pos);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) band_add_w(band, w[e]);
+            }
+        }
+        band_flush(band, acc);  // 32 tokens per lane and block: far below a band's limit
     }
-    bad = f & 1u;
-    pos = (f >> 1) & 1u;
-    __syncthreads();
+    acc = dig_wave_sum(acc);
 }
 
 // inclusive scan of Dig over the 64 lanes
@@ -363,111 +383,75 @@ __device__ __forceinline__ Dig dig_wave_scan(Dig x) {
     return x;
 }
 
-// LDS slot of chunk token t: one pad word per 32 tokens, so that a lane
-// reading 32 contiguous tokens hits distinct banks
-__device__ __forceinline__ int vf_slot(int t) { return t + (t >> 5); }
-constexpr int VF_SLOTS = VF_L + VF_L / 32;
-
-// Smallest t in [a, a + len), len <= VF_L, whose prefix (from a) exceeds thr.
-// The chunk's weights are loaded coalesced into LDS; lane l of wave w then
-// owns tokens [32 (64 w + l), +32) and sums them.  The quarter that holds the
-// crossing is found from the wave sums, the lane from one scan of that wave's
-// lane sums, the token from one scan of that lane's 32 weights.  Every thread
-// gets t.
+// Smallest t in [a, a + len), len <= VF_QMAX, whose prefix (from a) exceeds
+// thr; the range's weights are valid and their sum exceeds thr.  Thread i
+// takes tokens [a + 8 i, +8) (one load round for the whole range); a
+// workgroup scan of the thread sums finds the thread, which then walks its 8
+// tokens.  Every thread gets t.
 template <bool VEC>
-__device__ int wg_search_chunk(const WRow& r, int a, int len, const Nat& thr, Dig* sh_dig, int* sh_int, Nat* sh_nat,
-                               float* sh_w) {
-    constexpr int TPL = VF_L / VF_THREADS;  // tokens per lane: 32
+__device__ int wg_search_quarter(const WRow& r, int a, int len, const Nat& thr, Dig* sh_dig, int* sh_int) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (VEC && len == VF_L) {
-        f32x4 qv[VF_SPT], pv[VF_SPT];
+    const int ta = a + 8 * tid, e_end = a + len;
+    float w[8];
+    if (VEC && ta + 8 <= e_end) {
 #pragma unroll
-        for (int k = 0; k < VF_SPT; ++k) {
-            const int i = a + 4 * tid + 4 * VF_THREADS * k;
-            qv[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r.q + i));
-            pv[k] = r.mode == 0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r.p + i)) : qv[k];
-        }
-#pragma unroll
-        for (int k = 0; k < VF_SPT; ++k) {
-            float* dst = sh_w + vf_slot(4 * tid + 4 * VF_THREADS * k);  // 4 tokens, one 32-run
+        for (int h = 0; h < 2; ++h) {
+            const f32x4 qv = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r.q + ta + 4 * h));
+            const f32x4 pv =
+                r.mode == 0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r.p + ta + 4 * h)) : qv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const float x = r.mode == 0 ? qv[k][e] - pv[k][e] : qv[k][e];
-                dst[e] = x > 0.0f ? x : 0.0f;  // the row is valid: max(d, 0)
+                const float x = r.mode == 0 ? qv[e] - pv[e] : qv[e];
+                w[4 * h + e] = x > 0.0f ? x : 0.0f;  // the row is valid: max(d, 0)
             }
         }
     } else {
-        for (int t0 = 0; t0 < VF_L; t0 += 8 * VF_THREADS) {
-            float x[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = t0 + tid + VF_THREADS * e, i = a + t;
-                x[e] = t < len ? (r.mode == 0 ? r.q[i] - r.p[i] : r.q[i]) : 0.0f;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sh_w[vf_slot(t0 + tid + VF_THREADS * e)] = x[e] > 0.0f ? x[e] : 0.0f;
+        for (int e = 0; e < 8; ++e) {
+            const int i = ta + e;
+            const float x = i < e_end ? (r.mode == 0 ? r.q[i] - r.p[i] : r.q[i]) : 0.0f;
+            w[e] = x > 0.0f ? x : 0.0f;
         }
     }
-    if (tid == 0) sh_int[1] = -1;
-    __syncthreads();
-    Dig lsum;
-    dig_zero(lsum);
+    Dig mine;
+    dig_zero(mine);
     {
         Band band;
         band_zero(band);
-        const float* lw = sh_w + (TPL + 1) * tid;  // = vf_slot(TPL * tid)
 #pragma unroll
-        for (int e = 0; e < TPL; ++e) band_add_w(band, lw[e]);
-        band_flush(band, lsum);
+        for (int e = 0; e < 8; ++e) band_add_w(band, w[e]);
+        band_flush(band, mine);
     }
-    const Dig wsum = dig_wave_sum(lsum);
-    if (lane == 0) sh_dig[wave] = wsum;
+    Dig inc = dig_wave_scan(mine);
+    if (lane == 63) sh_dig[wave] = inc;
+    if (tid == 0) sh_int[4] = VF_THREADS - 1;
     __syncthreads();
-    if (tid == 0) {
-        Dig cum;
-        dig_zero(cum);
-        int ws = VF_THREADS / 64 - 1;
-        Nat rem = thr;
-        for (int q = 0; q < VF_THREADS / 64; ++q) {
-            Dig next = cum;
-            dig_add(next, sh_dig[q]);
-            if (nat_gt(nat_of(next), thr)) {
-                ws = q;
-                rem = nat_sub(thr, nat_of(cum));
+#pragma unroll
+    for (int v = 0; v < VF_THREADS / 64 - 1; ++v)
+        if (v < wave) dig_add(inc, sh_dig[v]);
+    const uint64_t hit = __ballot(nat_gt(nat_of(inc), thr));
+    if (lane == 0 && hit) atomicMin(&sh_int[4], wave * 64 + (int)__builtin_ctzll(hit));
+    __syncthreads();
+    if (tid == sh_int[4]) {
+        Dig run = inc;  // step back to the exclusive prefix, then add token by token
+#pragma unroll
+        for (int k = 0; k < VF_ND; ++k) run.d[k] -= mine.d[k];
+        int t = ta + 7;
+#pragma unroll 1
+        for (int e = 0; e < 8; ++e) {
+            float we = w[0];  // w[e] without indexing registers dynamically
+#pragma unroll
+            for (int k = 1; k < 8; ++k) we = e == k ? w[k] : we;
+            dig_add_w(run, we);
+            if (nat_gt(nat_of(run), thr)) {
+                t = ta + e;
                 break;
             }
-            cum = next;
         }
-        sh_int[0] = ws;
-        sh_nat[0] = rem;
+        sh_int[5] = t;
     }
     __syncthreads();
-    const int ws = sh_int[0];
-    if (wave == ws) {
-        const Nat rem = sh_nat[0];
-        // the lane: first whose inclusive prefix exceeds rem
-        const Dig inc = dig_wave_scan(lsum);
-        const uint64_t hit = __ballot(nat_gt(nat_of(inc), rem));
-        const int L = hit ? (int)__builtin_ctzll(hit) : 63;
-        Dig ex = inc;
-#pragma unroll
-        for (int k = 0; k < VF_ND; ++k) ex.d[k] -= lsum.d[k];
-        // rem2 = rem - (exclusive prefix of lane L), broadcast from lane L
-        Nat r2 = nat_sub(rem, nat_of(ex));
-#pragma unroll
-        for (int k = 0; k <= VF_NN; ++k) r2.n[k] = __shfl(r2.n[k], L, 64);
-        // the token: lanes 0..31 take lane L's tokens
-        const int t0 = TPL * (64 * ws + L);
-        const float w = lane < TPL ? sh_w[vf_slot(t0 + lane)] : 0.0f;
-        Dig mine;
-        dig_zero(mine);
-        dig_add_w(mine, w);
-        const Dig tinc = dig_wave_scan(mine);
-        const uint64_t thit = __ballot(lane < TPL && nat_gt(nat_of(tinc), r2));
-        if (lane == 0) sh_int[1] = a + t0 + (thit ? (int)__builtin_ctzll(thit) : TPL - 1);
-    }
-    __syncthreads();
-    return sh_int[1];
+    return sh_int[5];
 }
 
 // Smallest t in [a, a + len) whose prefix (from a) exceeds thr; the range's
@@ -576,10 +560,9 @@ template <bool VEC>
 __global__ __launch_bounds__(VF_THREADS) void verify_kernel(VerifyArgs a) {
     __shared__ Dig sh_dig[VF_THREADS / 64];
     __shared__ uint32_t sh_flag[VF_THREADS / 64];
-    __shared__ int sh_int[4];
+    __shared__ int sh_int[8];
     __shared__ Nat sh_nat[1];
-    __shared__ float sh_w[VF_SLOTS];  // the searched chunk's weights (last arriver)
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.x / a.C, c = blockIdx.x - b * a.C;
     const int N = a.N, V = a.V;
 
@@ -604,20 +587,24 @@ __global__ __launch_bounds__(VF_THREADS) void verify_kernel(VerifyArgs a) {
     row.p = j < N ? a.p + ((size_t)b * N + j) * V : nullptr;
     row.mode = j < N ? 0 : 1;
 
-    // ---- this chunk's exact sum and flags, published
-    const int ca = c * a.L, clen = min(a.L, V - ca);
-    Dig sum;
-    uint32_t bad = 0, pos = 0;
-    if (VEC && a.L == VF_L && clen == VF_L) wg_chunk_sum(row, ca, sum, bad, pos, sh_dig, sh_flag);
-    else wg_range_sum<VEC>(row, ca, clen, sum, bad, pos, sh_dig, sh_flag);
-    uint64_t* rec = a.rec + ((size_t)b * a.C + c) * 8;
-    if (tid < VF_ND) {
-        uint64_t v = 0;  // sum.d[tid] without indexing registers dynamically
+    // ---- wave w: exact sum and flags of quarter w of this chunk, published
+    const int Q = a.L / 4;
+    {
+        const int qa = c * a.L + wave * Q;
+        const int qlen = max(0, min(Q, V - qa));
+        Dig qs;
+        uint32_t bad = 0, pos = 0;
+        wave_range_sum<VEC>(row, qa, qlen, qs, bad, pos);
+        const uint64_t fl = (__any(bad) ? 1u : 0u) | (__any(pos) ? 2u : 0u);
+        uint64_t* rec = a.rec + ((size_t)b * a.C + c) * VF_REC;
+        if (lane < VF_ND) {
+            uint64_t v = 0;  // qs.d[lane] without indexing registers dynamically
 #pragma unroll
-        for (int k = 0; k < VF_ND; ++k) v = tid == k ? sum.d[k] : v;
-        __hip_atomic_store(rec + tid, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int k = 0; k < VF_ND; ++k) v = lane == k ? qs.d[k] : v;
+            __hip_atomic_store(rec + VF_ND * wave + lane, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (lane == VF_ND) __hip_atomic_store(rec + 4 * VF_ND + wave, fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (tid == VF_ND) __hip_atomic_store(rec + VF_ND, (uint64_t)(bad | (pos << 1)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
@@ -631,24 +618,28 @@ __global__ __launch_bounds__(VF_THREADS) void verify_kernel(VerifyArgs a) {
     if (tid == 0) __hip_atomic_store(a.counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const float u = a.u_res[b];
     int result = -1;
-    // every chunk's record, one per thread (the plan keeps C <= 256): totals,
-    // flags, and the inclusive prefix over the chunks in order
-    const int lane = tid & 63, wave = tid >> 6;
+    // thread c < C: chunk c's record (the plan keeps C <= 256): its four
+    // quarter sums (kept for the quarter pick), their total and the flags;
+    // then the inclusive prefix over the chunks in order
+    Dig qsum[4];
+    uint32_t myfl = 0;
     Dig mine;
     dig_zero(mine);
-    uint32_t myfl = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) dig_zero(qsum[w]);
     if (tid < a.C) {
-        const uint64_t* rc = a.rec + ((size_t)b * a.C + tid) * 8;
+        const uint64_t* rc = a.rec + ((size_t)b * a.C + tid) * VF_REC;
 #pragma unroll
-        for (int k = 0; k < VF_ND; ++k) mine.d[k] = __hip_atomic_load(rc + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        myfl = (uint32_t)__hip_atomic_load(rc + VF_ND, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    Dig inc = mine;
+        for (int w = 0; w < 4; ++w) {
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const Dig up = dig_shfl_up(inc, o);
-        if (lane >= o) dig_add(inc, up);
+            for (int k = 0; k < VF_ND; ++k)
+                qsum[w].d[k] = __hip_atomic_load(rc + VF_ND * w + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            myfl |= (uint32_t)__hip_atomic_load(rc + 4 * VF_ND + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) dig_add(mine, qsum[w]);
     }
+    Dig inc = dig_wave_scan(mine);
     const uint32_t wfl = (__any(myfl & 1u) ? 1u : 0u) | (__any(myfl & 2u) ? 2u : 0u);
     if (lane == 63) {
         sh_dig[wave] = inc;
@@ -669,7 +660,8 @@ __global__ __launch_bounds__(VF_THREADS) void verify_kernel(VerifyArgs a) {
     if (!u_ok || (fl & 1u)) {
         // invalid weights or u_res: no token
     } else if (fl & 2u) {
-        // the chunk that holds the crossing: the first whose inclusive prefix exceeds the threshold
+        // the chunk that holds the crossing: the first whose inclusive prefix
+        // exceeds the threshold; its thread picks the quarter the same way
         const Nat thr = nat_mul_u(nat_of(tot), u);
         const bool over = tid < a.C && nat_gt(nat_of(inc), thr);
         if (tid == 0) sh_int[0] = a.C - 1;
@@ -679,17 +671,35 @@ __global__ __launch_bounds__(VF_THREADS) void verify_kernel(VerifyArgs a) {
         __syncthreads();
         const int cs = sh_int[0];
         if (tid == cs) {
-            Dig ex = inc;
+            Dig run = inc;
 #pragma unroll
-            for (int k = 0; k < VF_ND; ++k) ex.d[k] -= mine.d[k];
-            sh_nat[0] = nat_sub(thr, nat_of(ex));
+            for (int k = 0; k < VF_ND; ++k) run.d[k] -= mine.d[k];
+            int qsel = 3;
+            bool found = false;
+            Nat rem = nat_sub(thr, nat_of(run));
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                if (!found) {
+                    Dig nx = run;
+                    dig_add(nx, qsum[w]);
+                    if (nat_gt(nat_of(nx), thr) || w == 3) {
+                        found = true;
+                        qsel = w;
+                        rem = nat_sub(thr, nat_of(run));
+                    }
+                    run = nx;
+                }
+            }
+            sh_int[1] = qsel;
+            sh_nat[0] = rem;
         }
         __syncthreads();
+        const int qsel = sh_int[1];
         const Nat rem = sh_nat[0];
         __syncthreads();
-        const int sa = cs * a.L, slen = min(a.L, V - sa);
-        result = a.L == VF_L ? wg_search_chunk<VEC>(row, sa, slen, rem, sh_dig, sh_int, sh_nat, sh_w)
-                             : wg_search(row, sa, slen, rem, sh_dig, sh_int, sh_nat);
+        const int sa = cs * a.L + qsel * Q, slen = min(Q, V - sa);
+        result = Q <= VF_QMAX ? wg_search_quarter<VEC>(row, sa, slen, rem, sh_dig, sh_int)
+                              : wg_search(row, sa, slen, rem, sh_dig, sh_int, sh_nat);
     } else if (row.mode == 0) {
         // the residual is all zero: draw from q_j over the whole row
         WRow qr = row;
@@ -711,20 +721,21 @@ __global__ __launch_bounds__(VF_THREADS) void verify_kernel(VerifyArgs a) {
 VerifyPlan plan_verify(int B, int N, int V) {
     VerifyPlan p;
     if (B < 1 || N < 1 || N > VERIFY_MAX_N || V < 1) return p;
-    // chunks of VF_L tokens (the last arriver searches one chunk), at most
-    // one per thread of the last arriver
-    long long L = VF_L;
-    while ((V + L - 1) / L > VF_THREADS) L *= 2;
-    const long long C = (V + L - 1) / L;
+    // chunks of 2048 to 8192 tokens (a quarter per wave), larger only when a
+    // row would need more than one chunk per thread of the last arriver;
+    // small batches take small chunks so that more CUs share each row
+    long long L = 2048;
+    auto chunks = [&](long long l) { return (V + l - 1) / l; };
+    while (chunks(L) > VF_THREADS || (L < 8192 && (long long)B * chunks(L) > VERIFY_TARGET_WGS)) L *= 2;
+    const long long C = chunks(L);
     p.C = (int)C;
     p.L = (int)L;
-    p.rec_bytes = (size_t)B * C * 8 * sizeof(uint64_t);
+    p.rec_bytes = (size_t)B * C * VF_REC * sizeof(uint64_t);
     p.ok = (long long)B * C <= 0x7fffffffLL;
     return p;
 }
-
 hipError_t launch_verify(const VerifyArgs& a, const VerifyPlan& p, bool vec, hipStream_t st) {
-    if (!p.ok || a.C != p.C || a.L != p.L || a.C > VF_THREADS || a.N < 1 || a.N > VERIFY_MAX_N ||
+    if (!p.ok || a.C != p.C || a.L != p.L || a.C > VF_THREADS || a.N < 1 || a.N > VERIFY_MAX_N || a.L % 2048 ||
         (long long)a.C * a.L < a.V)
         return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((long long)a.B * a.C);

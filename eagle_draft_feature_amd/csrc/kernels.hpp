@@ -127,6 +127,7 @@ hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan& p, hipStream_
 
 // ------------------------------------------------------------ verify / accept
 constexpr int VERIFY_MAX_N = 64;  // drafts per sequence (one wave decides them)
+constexpr long long VERIFY_TARGET_WGS = 256;  // chunk size grows (up to 8192 tokens) past one workgroup per CU
 struct VerifyArgs {
     const float* p;        // [B, N, V]
     const float* q;        // [B, N + 1, V]

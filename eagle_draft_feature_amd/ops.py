@@ -265,6 +265,15 @@ def verify_accept(p: torch.Tensor, q: torch.Tensor, draft: torch.Tensor, u_acc: 
     return n_accepted, next_token
 
 
+def verify_chunking(B: int, N: int, V: int):
+    """eagle31_verify_chunking: (chunks per row, tokens per chunk) of eagle31_verify_accept."""
+    import ctypes
+    c = ctypes.c_int32(0)
+    t = ctypes.c_int32(0)
+    check("eagle31_verify_chunking", lib().eagle31_verify_chunking(B, N, V, ctypes.byref(c), ctypes.byref(t)))
+    return c.value, t.value
+
+
 def release() -> None:
     check("eagle31_release", lib().eagle31_release())
 

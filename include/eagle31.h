@@ -266,6 +266,18 @@ int eagle31_verify_accept(const float* p, const float* q, const int32_t* draft, 
                           const float* u_res, int64_t B, int64_t N, int64_t V, int32_t* n_accepted,
                           int32_t* next_token, void* stream);
 
+/*
+ * eagle31_verify_chunking - how eagle31_verify_accept splits a row: into
+ * *chunks pieces of *tokens_per_chunk tokens (the last may be shorter), one
+ * workgroup each, every workgroup summing a quarter per wave.  Pieces are
+ * 2048, 4096 or 8192 tokens: the smallest that keeps B * chunks at or below
+ * 256 workgroups (one per CU), else 8192; never more than 256 chunks per row
+ * (longer rows take larger pieces).  Host arithmetic only; no device memory is touched.
+ * Returns EAGLE31_ERR_SHAPE for the shapes eagle31_verify_accept rejects
+ * (B must be >= 1 here), EAGLE31_ERR_NULL for a NULL output pointer.
+ */
+int eagle31_verify_chunking(int64_t B, int64_t N, int64_t V, int32_t* chunks, int32_t* tokens_per_chunk);
+
 /* Human-readable name of a status code (static string). */
 const char* eagle31_status_string(int status);
 

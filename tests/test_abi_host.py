@@ -209,3 +209,82 @@ def _ecat(tok=0x700000, M=64, d=4096, vocab=16, e=WP, f=H1, dst=OUT, bad=None):
 ])
 def test_embed_concat_rejects_bad_arguments(kw, code):
     assert _ecat(**kw) == code
+
+
+# verify / accept: fake device addresses, 16-byte aligned; B=4, N=2, V=1000
+VP, VQ, VD, VUA, VUR, VN, VT = 0x1000000, 0x2000000, 0x3000000, 0x3100000, 0x3200000, 0x3300000, 0x3400000
+
+
+def _verify(**kw):
+    a = dict(p=VP, q=VQ, d=VD, ua=VUA, ur=VUR, B=4, N=2, V=1000, n=VN, t=VT)
+    a.update(kw)
+    return e31.lib().eagle31_verify_accept(a["p"], a["q"], a["d"], a["ua"], a["ur"], a["B"], a["N"], a["V"], a["n"],
+                                           a["t"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), _capi.ERR_SHAPE),
+    (dict(B=4097), _capi.ERR_SHAPE),
+    (dict(N=0), _capi.ERR_SHAPE),
+    (dict(N=65), _capi.ERR_SHAPE),
+    (dict(V=0), _capi.ERR_SHAPE),
+    (dict(V=(1 << 26) + 1), _capi.ERR_SHAPE),
+    (dict(p=None), _capi.ERR_NULL),
+    (dict(ur=None), _capi.ERR_NULL),
+    (dict(t=None), _capi.ERR_NULL),
+    (dict(q=VQ + 2), _capi.ERR_ALIGN),
+    (dict(d=VD + 1), _capi.ERR_ALIGN),
+    (dict(n=VN + 2), _capi.ERR_ALIGN),
+    (dict(n=VP + 4 * 1000), _capi.ERR_ALIAS),     # inside p
+    (dict(t=VQ + 8), _capi.ERR_ALIAS),            # inside q
+    (dict(t=VN + 8), _capi.ERR_ALIAS),            # overlaps n_accepted
+    (dict(n=VUA + 4), _capi.ERR_ALIAS),           # inside u_acc
+    (dict(B=0, p=None, t=None), _capi.OK),        # nothing to do
+])
+def test_verify_accept_rejects_bad_arguments(kw, code):
+    assert _verify(**kw) == code
+
+
+def _chunking(B, N, V):
+    c, t = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    st = e31.lib().eagle31_verify_chunking(B, N, V, ctypes.byref(c), ctypes.byref(t))
+    return st, c.value, t.value
+
+
+@pytest.mark.parametrize("B,N,V,want", [
+    (64, 4, 32000, (4, 8192)),
+    (64, 4, 128256, (16, 8192)),
+    (64, 4, 151936, (19, 8192)),
+    (16, 4, 32000, (16, 2048)),
+    (8, 4, 128256, (32, 4096)),
+    (1, 1, 2_100_000, (129, 16384)),
+    (1, 1, 5, (1, 2048)),
+    (4096, 1, 8192, (1, 8192)),
+])
+def test_verify_chunking_examples(B, N, V, want):
+    st, c, t = _chunking(B, N, V)
+    assert st == _capi.OK and (c, t) == want
+    assert e31.verify_chunking(B, N, V) == want
+
+
+def test_verify_chunking_rules():
+    """The chunk plan for a grid of shapes: pieces of 2048 * 2^k tokens that
+    cover the row, at most 256 per row; 8192 tokens at most unless the row
+    needs more than 256 pieces; the smallest piece that keeps B * chunks at or
+    below 256 (one workgroup per CU)."""
+    def C(V, L):
+        return -(-V // L)
+    for B in (1, 3, 64, 255, 1000, 4096):
+        for V in (1, 5, 2047, 2048, 2049, 32000, 128256, 151936, 262144, 524289, 2_100_000, 1 << 26):
+            st, c, L = _chunking(B, 4, V)
+            assert st == _capi.OK
+            assert L >= 2048 and L % 2048 == 0 and (L & (L - 1)) == 0
+            assert c == C(V, L) and (c - 1) * L < V <= c * L and c <= 256
+            if L > 8192:
+                assert C(V, L // 2) > 256
+            elif L > 2048:
+                assert C(V, L // 2) > 256 or B * C(V, L // 2) > 256
+    assert _chunking(0, 1, 10)[0] == _capi.ERR_SHAPE
+    assert _chunking(1, 0, 10)[0] == _capi.ERR_SHAPE
+    assert _chunking(1, 1, (1 << 26) + 1)[0] == _capi.ERR_SHAPE
+    assert e31.lib().eagle31_verify_chunking(1, 1, 10, None, ctypes.byref(ctypes.c_int32())) == _capi.ERR_NULL

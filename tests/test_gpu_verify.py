@@ -62,7 +62,7 @@ def check(p, q, draft, u_acc, u_res, what):
 
 @pytest.mark.parametrize("B,N,V,spread", [(64, 4, 32000, 0.5), (16, 8, 32000, 1.0), (8, 4, 128256, 0.5),
                                           (5, 3, 4099, 1.0), (3, 2, 1027, 0.3), (33, 1, 8191, 1.0),
-                                          (1, 64, 4096, 0.5), (7, 5, 5, 1.0)])
+                                          (1, 64, 4096, 0.5), (7, 5, 5, 1.0), (16, 3, 6143, 1.0)])
 def test_verify_random_batches(B, N, V, spread):
     note(f"verify random B={B} N={N} V={V}")
     p, q, draft, u_acc, u_res = synth.make_verify_inputs(B, N, V, seed=B * 1000 + V, spread=spread)
@@ -70,6 +70,23 @@ def test_verify_random_batches(B, N, V, spread):
     # repeatable
     n2, t2 = run(p, q, draft, u_acc, u_res)
     assert np.array_equal(n, n2)
+
+
+@pytest.mark.parametrize("B,N,V,L", [(8, 4, 128256, 4096), (64, 4, 151936, 8192), (2, 2, 2_100_000, 16384)])
+def test_verify_each_chunk_size(B, N, V, L):
+    """Rows split into 4096-, 8192- and 16384-token chunks (the last searches
+    its quarter with the general loop); rows are independent, so a sample of
+    them is checked against the oracle on the same inputs."""
+    note(f"verify chunk size B={B} N={N} V={V}")
+    assert e31().verify_chunking(B, N, V) == (-(-V // L), L)
+    p, q, draft, u_acc, u_res = synth.make_verify_inputs(B, N, V, seed=V + B, spread=0.5)
+    n, t = run(p, q, draft, u_acc, u_res)
+    rows = np.unique(np.concatenate([[0, B - 1], np.random.default_rng(V).choice(B, min(B, 14), replace=False)]))
+    n_o, t_o = oracle.verify_accept(p[rows], q[rows], draft[rows], u_acc[rows], u_res[rows])
+    print(f"[verify] chunk size {L}: rows {rows.tolist()} kept {n[rows].tolist()} emitted {t[rows].tolist()}", flush=True)
+    assert np.array_equal(n[rows], n_o), (n[rows], n_o)
+    assert np.array_equal(t[rows], t_o), (t[rows], t_o)
+    assert (t[rows] >= 0).all()
 
 
 def test_verify_q_equals_p_keeps_every_draft():
