@@ -12,10 +12,10 @@ from __future__ import annotations
 
 from ._capi import (NORM_LAYERNORM, NORM_NONE, NORM_RMSNORM, Eagle31Error, LIB_PATH, lib)
 from .ops import (debug_fail_workspace_zero, debug_stats_recompute, embed_concat, fold_prepare, fuse, fuse_folded,
-                  fuse_folded_noalloc, fuse_ws, noalloc_scratch_bytes, norm_kind, norm_output, release, row_stats,
+                  fuse_folded_noalloc, fuse_folded_rows, fuse_rows, fuse_ws, noalloc_scratch_bytes, norm_kind, norm_output, release, row_stats,
                   verify_accept, verify_chunking, workspace_init, workspace_size)
 
 __all__ = [
     "debug_fail_workspace_zero", "fuse_folded_noalloc", "noalloc_scratch_bytes", "NORM_NONE", "NORM_LAYERNORM", "NORM_RMSNORM", "Eagle31Error", "LIB_PATH", "lib", "fuse", "fuse_ws",
-    "fold_prepare", "fuse_folded", "row_stats", "workspace_size", "workspace_init", "release", "norm_kind", "norm_output", "embed_concat", "debug_stats_recompute", "verify_accept", "verify_chunking",
+    "fold_prepare", "fuse_folded", "fuse_rows", "fuse_folded_rows", "row_stats", "workspace_size", "workspace_init", "release", "norm_kind", "norm_output", "embed_concat", "debug_stats_recompute", "verify_accept", "verify_chunking",
 ]

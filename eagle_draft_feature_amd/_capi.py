@@ -55,6 +55,10 @@ SIGNATURES = {
     "eagle31_fuse_ws": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _f32, _pp, _pp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "eagle31_fold_prepare": (_int, [_i64, _int, _pp, _pp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "eagle31_fuse_folded": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _f32, _vp, _vp, _vp, _vp, _vp]),
+    "eagle31_fuse_rows": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _f32, _pp, _pp, _vp, _vp, _vp,
+                                 _i64, _vp]),
+    "eagle31_fuse_folded_rows": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int, _f32, _vp, _vp, _vp, _vp,
+                                        _i64, _vp]),
     "eagle31_fuse_folded_ws": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _f32, _vp, _vp, _vp, _vp, _vp, _sz,
                                       _vp]),
     "eagle31_fuse_folded_noalloc": (_int, [_vp, _vp, _vp, _i64, _i64, _int, _f32, _vp, _vp, _vp, _vp, _vp]),

@@ -65,13 +65,49 @@ int check_params(int64_t d, int norm_kind, const void* const* gamma, const void*
     return EAGLE31_OK;
 }
 
-int check_io(int64_t M, int64_t d, const void* h0, const void* h1, const void* h2, const void* out) {
+// Where a call's rows are (see RowView), with the byte extents the alias
+// checks use: state s spans ((n_src - 1) ld_s + d) elements from h_s, the
+// output ((M - 1) ld_out + d) from out.
+struct Rows {
+    const void* h[3] = {nullptr, nullptr, nullptr};
+    RowView rv;
+    size_t hext[3] = {0, 0, 0}, oext = 0, iext = 0;
+};
+constexpr int64_t MAX_LD = (int64_t)1 << 22;  // elements between rows, at most
+
+int check_rows(int64_t M, int64_t d, const void* h0, const void* h1, const void* h2, const int64_t* ld,
+               const int32_t* row_index, int64_t n_src, const void* out, int64_t ld_out, Rows& R) {
     if (M == 0) return EAGLE31_OK;
     if (h0 == nullptr || h1 == nullptr || h2 == nullptr || out == nullptr) return EAGLE31_ERR_NULL;
-    if (!aligned16(h0) || !aligned16(h1) || !aligned16(h2) || !aligned16(out)) return EAGLE31_ERR_ALIGN;
-    const size_t hb = (size_t)M * (size_t)d * 2;
-    if (overlaps(out, hb, h0, hb) || overlaps(out, hb, h1, hb) || overlaps(out, hb, h2, hb)) return EAGLE31_ERR_ALIAS;
+    const void* h[3] = {h0, h1, h2};
+    for (int s = 0; s < 3; ++s) {
+        const int64_t l = ld ? ld[s] : d;
+        if (l < d || l > MAX_LD || (l % 8) != 0) return EAGLE31_ERR_SHAPE;
+        R.h[s] = h[s];
+        R.rv.ld[s] = l;
+    }
+    if (ld_out < d || ld_out > MAX_LD || (ld_out % 8) != 0) return EAGLE31_ERR_SHAPE;
+    if (n_src < 1 || n_src > INT32_MAX || (row_index == nullptr && n_src < M)) return EAGLE31_ERR_SHAPE;
+    // an index reaches any row: its byte offset in a state buffer stays below 2^32
+    if (row_index != nullptr)
+        for (int s = 0; s < 3; ++s)
+            if ((uint64_t)n_src * (uint64_t)R.rv.ld[s] * 2 > ((uint64_t)1 << 32)) return EAGLE31_ERR_SHAPE;
+    if (!aligned16(h0) || !aligned16(h1) || !aligned16(h2) || !aligned16(out) || ((uintptr_t)row_index & 3u) != 0)
+        return EAGLE31_ERR_ALIGN;
+    R.rv.ld_out = ld_out;
+    R.rv.idx = row_index;
+    R.rv.n_src = (int)n_src;
+    for (int s = 0; s < 3; ++s) R.hext[s] = (size_t)((n_src - 1) * R.rv.ld[s] + d) * 2;
+    R.oext = (size_t)((M - 1) * ld_out + d) * 2;
+    R.iext = row_index ? (size_t)M * 4 : 0;
+    for (int s = 0; s < 3; ++s)
+        if (overlaps(out, R.oext, h[s], R.hext[s])) return EAGLE31_ERR_ALIAS;
+    if (overlaps(out, R.oext, row_index, R.iext)) return EAGLE31_ERR_ALIAS;
     return EAGLE31_OK;
+}
+
+int check_io(int64_t M, int64_t d, const void* h0, const void* h1, const void* h2, const void* out, Rows& R) {
+    return check_rows(M, d, h0, h1, h2, nullptr, nullptr, M > 0 ? M : 1, out, d, R);
 }
 
 // ------------------------------------------------------------- workspace
@@ -237,13 +273,13 @@ T* at(void* base, size_t off) {
 }
 
 // ------------------------------------------------------------- dispatch
-int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t d, int norm, float eps,
-             const void* const* gamma, const void* const* beta, const void* W, const void* bias, const void* wt,
-             const float* u, const float* c, bool folded, void* out, void* ws, size_t ws_bytes, hipStream_t st) {
+int run_fuse(const Rows& R, int64_t M, int64_t d, int norm, float eps, const void* const* gamma,
+             const void* const* beta, const void* W, const void* bias, const void* wt, const float* u, const float* c,
+             bool folded, void* out, void* ws, size_t ws_bytes, hipStream_t st) {
     const WsLayout L = layout_for(M, d, norm, folded);
     if (ws_bytes < L.total) return EAGLE31_ERR_WORKSPACE;
-    const uint16_t* h[3] = {static_cast<const uint16_t*>(h0), static_cast<const uint16_t*>(h1),
-                            static_cast<const uint16_t*>(h2)};
+    const uint16_t* h[3] = {static_cast<const uint16_t*>(R.h[0]), static_cast<const uint16_t*>(R.h[1]),
+                            static_cast<const uint16_t*>(R.h[2])};
     const uint16_t* g[3] = {nullptr, nullptr, nullptr};
     const uint16_t* b[3] = {nullptr, nullptr, nullptr};
     if (!folded && norm != NORM_NONE && gamma != nullptr)
@@ -261,6 +297,7 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
         a.u = u;
         a.c = c;
         a.out = static_cast<uint16_t*>(out);
+        a.rv = R.rv;
         a.M = (int)M;
         a.d = (int)d;
         a.eps = eps;
@@ -287,6 +324,7 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
         a.W = static_cast<const uint16_t*>(W);
         a.bias = static_cast<const uint16_t*>(bias);
         a.out = static_cast<uint16_t*>(out);
+        a.rv = R.rv;
         a.M = (int)M;
         a.d = (int)d;
         a.eps = eps;
@@ -305,7 +343,7 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
     float* mu = at<float>(ws, L.mu);
     float* rstd = at<float>(ws, L.rstd);
     if (norm != NORM_NONE) {
-        e = launch_row_stats(h[0], h[1], h[2], (int)M, (int)d, norm, eps, mu, rstd, st);
+        e = launch_row_stats(h[0], h[1], h[2], R.rv, (int)M, (int)d, norm, eps, mu, rstd, st);
         if (e != hipSuccess) return hip_fail(e);
     }
     if (!folded) {
@@ -327,6 +365,7 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
     a.mu = mu;
     a.rstd = rstd;
     a.out = static_cast<uint16_t*>(out);
+    a.rv = R.rv;
     a.M = (int)M;
     a.d = (int)d;
     a.norm = norm;
@@ -337,18 +376,16 @@ int run_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t 
     return EAGLE31_OK;
 }
 
-int validate_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int64_t d, int norm, float eps,
-                  const void* const* gamma, const void* const* beta, const void* W, const void* bias, void* out) {
-    int r = check_common(M, d, norm, eps);
-    if (r != EAGLE31_OK) return r;
+// The rows are checked by the caller (check_io or check_rows) after
+// check_common; these check the rest.
+int validate_fuse_params(const Rows& R, int64_t M, int64_t d, int norm, const void* const* gamma,
+                         const void* const* beta, const void* W, const void* bias, void* out) {
     if (W == nullptr) return EAGLE31_ERR_NULL;
     if (!aligned16(W) || (bias != nullptr && !aligned16(bias))) return EAGLE31_ERR_ALIGN;
-    r = check_params(d, norm, gamma, beta);
-    if (r != EAGLE31_OK) return r;
-    r = check_io(M, d, h0, h1, h2, out);
+    int r = check_params(d, norm, gamma, beta);
     if (r != EAGLE31_OK) return r;
     if (M > 0) {
-        const size_t ob = (size_t)M * (size_t)d * 2;
+        const size_t ob = R.oext;
         if (overlaps(out, ob, W, (size_t)3 * d * d * 2) || overlaps(out, ob, bias, (size_t)d * 2)) return EAGLE31_ERR_ALIAS;
         for (int s = 0; s < 3; ++s) {
             if (gamma != nullptr && overlaps(out, ob, gamma[s], (size_t)d * 2)) return EAGLE31_ERR_ALIAS;
@@ -358,21 +395,39 @@ int validate_fuse(const void* h0, const void* h1, const void* h2, int64_t M, int
     return EAGLE31_OK;
 }
 
-int validate_folded(const void* h0, const void* h1, const void* h2, int64_t M, int64_t d, int norm, float eps,
-                    const void* wt, const float* u, const float* c, void* out) {
-    int r = check_common(M, d, norm, eps);
-    if (r != EAGLE31_OK) return r;
+int validate_folded_params(const Rows& R, int64_t M, int64_t d, const void* wt, const float* u, const float* c,
+                           void* out) {
     if (wt == nullptr || u == nullptr || c == nullptr) return EAGLE31_ERR_NULL;
     if (!aligned16(wt) || !aligned16(u) || !aligned16(c)) return EAGLE31_ERR_ALIGN;
-    r = check_io(M, d, h0, h1, h2, out);
-    if (r != EAGLE31_OK) return r;
     if (M > 0) {
-        const size_t ob = (size_t)M * (size_t)d * 2;
+        const size_t ob = R.oext;
         if (overlaps(out, ob, wt, (size_t)3 * d * d * 2) || overlaps(out, ob, u, (size_t)3 * d * 4) ||
             overlaps(out, ob, c, (size_t)d * 4))
             return EAGLE31_ERR_ALIAS;
     }
     return EAGLE31_OK;
+}
+
+// check_common, the rows (dense: contiguous [M, d] rows, else the row view
+// arguments), then the weight-side arguments
+int prep_fuse(bool dense, const void* h0, const void* h1, const void* h2, const int64_t* ld, const int32_t* idx,
+              int64_t n_src, int64_t M, int64_t d, int norm, float eps, const void* const* gamma,
+              const void* const* beta, const void* W, const void* bias, void* out, int64_t ld_out, Rows& R) {
+    int r = check_common(M, d, norm, eps);
+    if (r != EAGLE31_OK) return r;
+    r = dense ? check_io(M, d, h0, h1, h2, out, R) : check_rows(M, d, h0, h1, h2, ld, idx, n_src, out, ld_out, R);
+    if (r != EAGLE31_OK) return r;
+    return validate_fuse_params(R, M, d, norm, gamma, beta, W, bias, out);
+}
+
+int prep_folded(bool dense, const void* h0, const void* h1, const void* h2, const int64_t* ld, const int32_t* idx,
+                int64_t n_src, int64_t M, int64_t d, int norm, float eps, const void* wt, const float* u,
+                const float* c, void* out, int64_t ld_out, Rows& R) {
+    int r = check_common(M, d, norm, eps);
+    if (r != EAGLE31_OK) return r;
+    r = dense ? check_io(M, d, h0, h1, h2, out, R) : check_rows(M, d, h0, h1, h2, ld, idx, n_src, out, ld_out, R);
+    if (r != EAGLE31_OK) return r;
+    return validate_folded_params(R, M, d, wt, u, c, out);
 }
 
 }  // namespace
@@ -382,7 +437,9 @@ extern "C" {
 int eagle31_fuse(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d, int norm_kind,
                  float eps, const void* const* gamma, const void* const* beta, const void* W, const void* bias,
                  void* out, void* stream) {
-    int r = validate_fuse(h_low, h_mid, h_high, M, d, norm_kind, eps, gamma, beta, W, bias, out);
+    Rows R;
+    int r = prep_fuse(true, h_low, h_mid, h_high, nullptr, nullptr, 0, M, d, norm_kind, eps, gamma, beta, W, bias,
+                      out, d, R);
     if (r != EAGLE31_OK || M == 0) return r;
     hipStream_t st = static_cast<hipStream_t>(stream);
     std::lock_guard<std::mutex> lock(g_ws_mutex);
@@ -390,8 +447,24 @@ int eagle31_fuse(const void* h_low, const void* h_mid, const void* h_high, int64
     size_t wsb = 0;
     r = owned_workspace(layout_for(M, d, norm_kind, false).total, st, &ws, &wsb);
     if (r != EAGLE31_OK) return r;
-    return run_fuse(h_low, h_mid, h_high, M, d, norm_kind, eps, gamma, beta, W, bias, nullptr, nullptr, nullptr,
-                    false, out, ws, wsb, st);
+    return run_fuse(R, M, d, norm_kind, eps, gamma, beta, W, bias, nullptr, nullptr, nullptr, false, out, ws, wsb, st);
+}
+
+int eagle31_fuse_rows(const void* h_low, const void* h_mid, const void* h_high, const int64_t* ld,
+                      const int32_t* row_index, int64_t n_src, int64_t M, int64_t d, int norm_kind, float eps,
+                      const void* const* gamma, const void* const* beta, const void* W, const void* bias, void* out,
+                      int64_t ld_out, void* stream) {
+    Rows R;
+    int r = prep_fuse(false, h_low, h_mid, h_high, ld, row_index, n_src, M, d, norm_kind, eps, gamma, beta, W, bias,
+                      out, ld_out, R);
+    if (r != EAGLE31_OK || M == 0) return r;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    void* ws = nullptr;
+    size_t wsb = 0;
+    r = owned_workspace(layout_for(M, d, norm_kind, false).total, st, &ws, &wsb);
+    if (r != EAGLE31_OK) return r;
+    return run_fuse(R, M, d, norm_kind, eps, gamma, beta, W, bias, nullptr, nullptr, nullptr, false, out, ws, wsb, st);
 }
 
 size_t eagle31_workspace_size(int64_t M, int64_t d, int norm_kind) {
@@ -423,13 +496,15 @@ int eagle31_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
 int eagle31_fuse_ws(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d, int norm_kind,
                     float eps, const void* const* gamma, const void* const* beta, const void* W, const void* bias,
                     void* out, void* workspace, size_t ws_bytes, void* stream) {
-    int r = validate_fuse(h_low, h_mid, h_high, M, d, norm_kind, eps, gamma, beta, W, bias, out);
+    Rows R;
+    int r = prep_fuse(true, h_low, h_mid, h_high, nullptr, nullptr, 0, M, d, norm_kind, eps, gamma, beta, W, bias,
+                      out, d, R);
     if (r != EAGLE31_OK || M == 0) return r;
     if (workspace == nullptr) return EAGLE31_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return EAGLE31_ERR_ALIGN;
     if (ws_bytes < layout_for(M, d, norm_kind, false).total) return EAGLE31_ERR_WORKSPACE;
-    return run_fuse(h_low, h_mid, h_high, M, d, norm_kind, eps, gamma, beta, W, bias, nullptr, nullptr, nullptr,
-                    false, out, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+    return run_fuse(R, M, d, norm_kind, eps, gamma, beta, W, bias, nullptr, nullptr, nullptr, false, out, workspace,
+                    ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 int eagle31_fold_prepare(int64_t d, int norm_kind, const void* const* gamma, const void* const* beta, const void* W,
@@ -462,7 +537,9 @@ int eagle31_fold_prepare(int64_t d, int norm_kind, const void* const* gamma, con
 
 int eagle31_fuse_folded(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d, int norm_kind,
                         float eps, const void* w_folded, const float* u, const float* c, void* out, void* stream) {
-    int r = validate_folded(h_low, h_mid, h_high, M, d, norm_kind, eps, w_folded, u, c, out);
+    Rows R;
+    int r = prep_folded(true, h_low, h_mid, h_high, nullptr, nullptr, 0, M, d, norm_kind, eps, w_folded, u, c, out, d,
+                        R);
     if (r != EAGLE31_OK || M == 0) return r;
     hipStream_t st = static_cast<hipStream_t>(stream);
     std::lock_guard<std::mutex> lock(g_ws_mutex);
@@ -470,26 +547,48 @@ int eagle31_fuse_folded(const void* h_low, const void* h_mid, const void* h_high
     size_t wsb = 0;
     r = owned_workspace(layout_for(M, d, norm_kind, true).total, st, &ws, &wsb);
     if (r != EAGLE31_OK) return r;
-    return run_fuse(h_low, h_mid, h_high, M, d, norm_kind, eps, nullptr, nullptr, nullptr, nullptr, w_folded, u, c,
-                    true, out, ws, wsb, st);
+    return run_fuse(R, M, d, norm_kind, eps, nullptr, nullptr, nullptr, nullptr, w_folded, u, c, true, out, ws, wsb,
+                    st);
+}
+
+int eagle31_fuse_folded_rows(const void* h_low, const void* h_mid, const void* h_high, const int64_t* ld,
+                             const int32_t* row_index, int64_t n_src, int64_t M, int64_t d, int norm_kind, float eps,
+                             const void* w_folded, const float* u, const float* c, void* out, int64_t ld_out,
+                             void* stream) {
+    Rows R;
+    int r = prep_folded(false, h_low, h_mid, h_high, ld, row_index, n_src, M, d, norm_kind, eps, w_folded, u, c, out,
+                        ld_out, R);
+    if (r != EAGLE31_OK || M == 0) return r;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    void* ws = nullptr;
+    size_t wsb = 0;
+    r = owned_workspace(layout_for(M, d, norm_kind, true).total, st, &ws, &wsb);
+    if (r != EAGLE31_OK) return r;
+    return run_fuse(R, M, d, norm_kind, eps, nullptr, nullptr, nullptr, nullptr, w_folded, u, c, true, out, ws, wsb,
+                    st);
 }
 
 int eagle31_fuse_folded_ws(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d,
                            int norm_kind, float eps, const void* w_folded, const float* u, const float* c, void* out,
                            void* workspace, size_t ws_bytes, void* stream) {
-    int r = validate_folded(h_low, h_mid, h_high, M, d, norm_kind, eps, w_folded, u, c, out);
+    Rows R;
+    int r = prep_folded(true, h_low, h_mid, h_high, nullptr, nullptr, 0, M, d, norm_kind, eps, w_folded, u, c, out, d,
+                        R);
     if (r != EAGLE31_OK || M == 0) return r;
     if (workspace == nullptr) return EAGLE31_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return EAGLE31_ERR_ALIGN;
     if (ws_bytes < layout_for(M, d, norm_kind, true).total) return EAGLE31_ERR_WORKSPACE;
-    return run_fuse(h_low, h_mid, h_high, M, d, norm_kind, eps, nullptr, nullptr, nullptr, nullptr, w_folded, u, c,
-                    true, out, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+    return run_fuse(R, M, d, norm_kind, eps, nullptr, nullptr, nullptr, nullptr, w_folded, u, c, true, out, workspace,
+                    ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 int eagle31_fuse_folded_noalloc(const void* h_low, const void* h_mid, const void* h_high, int64_t M, int64_t d,
                                 int norm_kind, float eps, const void* w_folded, const float* u, const float* c,
                                 void* out, void* stream) {
-    int r = validate_folded(h_low, h_mid, h_high, M, d, norm_kind, eps, w_folded, u, c, out);
+    Rows R;
+    int r = prep_folded(true, h_low, h_mid, h_high, nullptr, nullptr, 0, M, d, norm_kind, eps, w_folded, u, c, out, d,
+                        R);
     if (r != EAGLE31_OK || M == 0) return r;
     const size_t need = layout_for(M, d, norm_kind, true).total;
     if (need > NOALLOC_SCRATCH_BYTES) return EAGLE31_ERR_TOO_LARGE;
@@ -497,8 +596,8 @@ int eagle31_fuse_folded_noalloc(const void* h_low, const void* h_mid, const void
     void* ws = nullptr;
     r = noalloc_scratch(st, &ws);
     if (r != EAGLE31_OK) return r;
-    return run_fuse(h_low, h_mid, h_high, M, d, norm_kind, eps, nullptr, nullptr, nullptr, nullptr, w_folded, u, c,
-                    true, out, ws, NOALLOC_SCRATCH_BYTES, st);
+    return run_fuse(R, M, d, norm_kind, eps, nullptr, nullptr, nullptr, nullptr, w_folded, u, c, true, out, ws,
+                    NOALLOC_SCRATCH_BYTES, st);
 }
 
 size_t eagle31_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
@@ -512,8 +611,8 @@ int eagle31_row_stats(const void* h_low, const void* h_mid, const void* h_high, 
     if (!aligned16(h_low) || !aligned16(h_mid) || !aligned16(h_high) || !aligned16(mu) || !aligned16(rstd))
         return EAGLE31_ERR_ALIGN;
     const hipError_t e = launch_row_stats(static_cast<const uint16_t*>(h_low), static_cast<const uint16_t*>(h_mid),
-                                          static_cast<const uint16_t*>(h_high), (int)M, (int)d, norm_kind, eps, mu,
-                                          rstd, static_cast<hipStream_t>(stream));
+                                          static_cast<const uint16_t*>(h_high), dense_rows((int)M, (int)d), (int)M,
+                                          (int)d, norm_kind, eps, mu, rstd, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e);
     return EAGLE31_OK;
 }
@@ -547,8 +646,8 @@ int eagle31_embed_concat(const int32_t* tokens, int64_t M, int64_t d, int64_t vo
     if (M < 0 || M > MAX_M || d <= 0 || d > EMBED_CONCAT_MAX_D || (d % 64) != 0 || vocab < 1 || vocab > INT32_MAX)
         return EAGLE31_ERR_SHAPE;
     if (M == 0) return EAGLE31_OK;
-    if (tokens == nullptr || embed == nullptr || fused == nullptr || dst == nullptr) return EAGLE31_ERR_NULL;
-    if (!aligned16(embed) || !aligned16(fused) || !aligned16(dst) || ((uintptr_t)tokens & 3u) != 0 ||
+    if (tokens == nullptr || embed == nullptr || dst == nullptr) return EAGLE31_ERR_NULL;
+    if (!aligned16(embed) || (fused != nullptr && !aligned16(fused)) || !aligned16(dst) || ((uintptr_t)tokens & 3u) != 0 ||
         ((uintptr_t)bad_count & 3u) != 0)
         return EAGLE31_ERR_ALIGN;
     const size_t db = (size_t)M * (size_t)d * 4, rb = (size_t)M * (size_t)d * 2;

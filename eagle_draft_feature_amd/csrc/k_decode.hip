@@ -132,6 +132,8 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
     const int t0c = (c * T) / ks, t1c = ((c + 1) * T) / ks;
     const int s_first = t0c / TS;
     const int npieces = (t1c - 1) / TS - s_first + 1;
+    // the tokens' source rows and valid mask (every wave holds all of them)
+    const WaveRows wr = rv_wave(a.rv, M);
 
     for (int pi = 0; pi < npieces; ++pi) {
         const int s = s_first + pi;
@@ -140,13 +142,15 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
         const uint16_t* __restrict__ hs = a.h[s];
         const uint16_t* __restrict__ gam = a.gamma[s];
         const uint16_t* __restrict__ bet = a.beta[s];
+        const size_t lds = (size_t)rv_ld(a.rv, s);
 
         // ---- provisional shift per token row: mean of the piece's first 32 values
+        const size_t shift_src = (size_t)rv_lane_src(wr, (tid >> 2) & 63);  // (every lane, before the branch)
         if (NORM == NORM_LN && tid < 4 * DECODE_MAX_M) {
             const int m = tid >> 2;
             if (m < M) {
                 const uint4 x =
-                    *reinterpret_cast<const uint4*>(hs + (size_t)m * d + (tp0 * 32 - seg_k0) + (tid & 3) * 8);
+                    *reinterpret_cast<const uint4*>(hs + shift_src * lds + (tp0 * 32 - seg_k0) + (tid & 3) * 8);
                 float v = bf_lo(x.x) + bf_hi(x.x) + bf_lo(x.y) + bf_hi(x.y) + bf_lo(x.z) + bf_hi(x.z) +
                           bf_lo(x.w) + bf_hi(x.w);
                 v += __shfl_xor(v, 1, 64);
@@ -171,7 +175,8 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
             gmk[tt] = (NORM == NORM_LN && m == M) ? 0xffffffffu : 0u;
             bmk[tt] = (NORM == NORM_LN && m == M + 1) ? 0xffffffffu : 0u;
             shift[tt] = (NORM == NORM_LN && is_tok) ? sh_shift[m] : 0.f;
-            arow[tt] = hs + (size_t)(is_tok ? m : 0) * d - seg_k0 + 8 * g;
+            const size_t src = (size_t)rv_lane_src(wr, min(m, 63));
+            arow[tt] = hs + (is_tok ? src : 0) * lds - seg_k0 + 8 * g;
         }
 
         f32x4 acc[MT][J];
@@ -483,7 +488,8 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
             }
             y += (NORM == NORM_NONE) ? ys : sh_r[ss][m] * ys;
         }
-        a.out[(size_t)m * d + n0 + n] = __builtin_bit_cast(uint16_t, (__bf16)(y + add));
+        a.out[(size_t)m * (size_t)a.rv.ld_out + n0 + n] =
+            rv_ok(wr, m) ? __builtin_bit_cast(uint16_t, (__bf16)(y + add)) : (uint16_t)0;
     }
     if (tid == 0) __hip_atomic_store(a.counters + b, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -569,10 +575,13 @@ __global__ __launch_bounds__(512) void decode_one_kernel(DecodeArgs a) {
 #pragma unroll
     for (int p = 0; p < R; ++p) rw[p] = load_w_nt<uint4>(wp + (size_t)p * wstep);
 
+    // the token's source row (an invalid index reads row 0; the output is zeros)
+    bool tok_ok;
+    const size_t src0 = (size_t)rv_src(a.rv, 0, tok_ok);
     // statistics of the three rows (waves 0..2)
     if (NORM != NORM_NONE && wave < 3) {
         float K, S1, S2;
-        one_row_sums(a.h[wave], d, lane, NORM == NORM_LN, K, S1, S2);
+        one_row_sums(a.h[wave] + src0 * (size_t)rv_ld(a.rv, wave), d, lane, NORM == NORM_LN, K, S1, S2);
         if (lane == 0) {
             const float inv_d = 1.0f / (float)d;
             float mu = 0.f, rstd;
@@ -591,7 +600,7 @@ __global__ __launch_bounds__(512) void decode_one_kernel(DecodeArgs a) {
     // xn of this chunk's rows, in fp32
     for (int r = tid; r < rows; r += 512) {
         const int k = k0 + r, s = k / d, kk = k - s * d;
-        const uint16_t* hs = s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2]);
+        const uint16_t* hs = (s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2])) + src0 * (size_t)rv_ld(a.rv, s);
         float x = bf_one(hs[kk]);
         if (NORM != NORM_NONE) {
             const uint16_t* gs = s == 0 ? a.gamma[0] : (s == 1 ? a.gamma[1] : a.gamma[2]);
@@ -662,7 +671,7 @@ __global__ __launch_bounds__(512) void decode_one_kernel(DecodeArgs a) {
                 if (c0 + q < nkc) y += v[q];
         }
         if (a.bias) y += bf_one(a.bias[n0 + tid]);
-        a.out[n0 + tid] = (uint16_t)(pack_bf2(y, 0.f) & 0xffffu);
+        a.out[n0 + tid] = tok_ok ? (uint16_t)(pack_bf2(y, 0.f) & 0xffffu) : (uint16_t)0;
     }
     if (tid == 0) __hip_atomic_store(a.counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -11,7 +11,9 @@
 // outside [0, vocab) reads row 0 as a stand-in, writes zeros instead and is
 // counted once (vector atomic) when a counter is given.  The fused feature
 // and the output are touched once (non-temporal hint); embedding rows may
-// repeat and stay ordinary loads.
+// repeat and stay ordinary loads.  Without a fused feature (F false) only the
+// embedding half is written: the fused kernels write the other half
+// themselves, through their output row stride.
 #include <algorithm>
 
 #include "common.hpp"
@@ -21,7 +23,7 @@ namespace e31 {
 
 constexpr int EC_WAVES = 8;
 
-template <int P>
+template <int P, bool F>
 __global__ __launch_bounds__(64 * EC_WAVES) void embed_concat_kernel(const int32_t* __restrict__ tokens, int M, int d,
                                                                      int vocab, const uint16_t* __restrict__ embed,
                                                                      const uint16_t* __restrict__ fused,
@@ -41,14 +43,14 @@ __global__ __launch_bounds__(64 * EC_WAVES) void embed_concat_kernel(const int32
         for (int i = 0; i < P; ++i) {
             const int vi = min(lane + 64 * i, nvec - 1);
             ev[i] = e[vi];
-            fv[i] = __builtin_nontemporal_load(&f[vi]);
+            if (F) fv[i] = __builtin_nontemporal_load(&f[vi]);
         }
         const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int i = 0; i < P; ++i) {
             const int vi = min(lane + 64 * i, nvec - 1);
             __builtin_nontemporal_store(ok ? ev[i] : zero, &o[vi]);
-            __builtin_nontemporal_store(fv[i], &o[nvec + vi]);
+            if (F) __builtin_nontemporal_store(fv[i], &o[nvec + vi]);
         }
         if (!ok && lane == 0 && bad_count != nullptr) atomicAdd(bad_count, 1);
     }
@@ -60,8 +62,15 @@ hipError_t launch_embed_concat(const int32_t* tokens, int M, int d, int vocab, c
     const int nvec = d / 8;
     const int need = (nvec + 63) / 64;
     const int grid = (int)std::min<int64_t>(((int64_t)M + EC_WAVES - 1) / EC_WAVES, 512);
-#define E31_EC(PP) \
-    embed_concat_kernel<PP><<<grid, 64 * EC_WAVES, 0, st>>>(tokens, M, d, vocab, embed, fused, dst, bad_count)
+#define E31_EC(PP)                                                                                                  \
+    do {                                                                                                           \
+        if (fused != nullptr)                                                                                      \
+            embed_concat_kernel<PP, true><<<grid, 64 * EC_WAVES, 0, st>>>(tokens, M, d, vocab, embed, fused, dst,   \
+                                                                          bad_count);                              \
+        else                                                                                                       \
+            embed_concat_kernel<PP, false><<<grid, 64 * EC_WAVES, 0, st>>>(tokens, M, d, vocab, embed, fused, dst,  \
+                                                                           bad_count);                             \
+    } while (0)
     if (need <= 1) E31_EC(1);
     else if (need <= 2) E31_EC(2);
     else if (need <= 4) E31_EC(4);

@@ -151,9 +151,11 @@ __device__ __forceinline__ void row_sums(const uint16_t* row, int d, int lane, f
     row_sums_pre<NORM>(row, d, lane, pre, K, S1, S2);
 }
 
-__device__ __forceinline__ const uint16_t* stats_row(const GemvArgs& a, int it) {
+// (state, token) row it = s M + m: token m's source row of state s
+__device__ __forceinline__ const uint16_t* stats_row(const GemvArgs& a, int it, const WaveRows& wr) {
     const int s = it / a.M, m = it - s * a.M;
-    return a.h[s] + (size_t)m * a.d;
+    const uint16_t* hs = s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2]);
+    return hs + (size_t)rv_lane_src(wr, m) * (size_t)rv_ld(a.rv, s);
 }
 
 // Producer side (one wave): rows first, first + stride, ... of the 3M
@@ -161,12 +163,13 @@ __device__ __forceinline__ const uint16_t* stats_row(const GemvArgs& a, int it) 
 // three sums are stored first, then, once they have completed, the id.
 // `pre` holds the preloaded start of row `first` (if first < 3M).
 template <int NORM>
-__device__ void stats_produce(const GemvArgs& a, int first, int stride, int lane, const RowPre& pre) {
+__device__ void stats_produce(const GemvArgs& a, int first, int stride, int lane, const RowPre& pre,
+                              const WaveRows& wr) {
     const int need = 3 * a.M;
     for (int it = first; it < need; it += stride) {
         float K, S1, S2;
-        if (it == first) row_sums_pre<NORM>(stats_row(a, it), a.d, lane, pre, K, S1, S2);
-        else row_sums<NORM>(stats_row(a, it), a.d, lane, K, S1, S2);
+        if (it == first) row_sums_pre<NORM>(stats_row(a, it, wr), a.d, lane, pre, K, S1, S2);
+        else row_sums<NORM>(stats_row(a, it, wr), a.d, lane, K, S1, S2);
         if (lane == 0) {
             uint32_t* rec = a.rstats + 4 * it;
             store_coherent_u32(rec + 0, __float_as_uint(K));
@@ -183,7 +186,7 @@ __device__ void stats_produce(const GemvArgs& a, int first, int stride, int lane
 // rows itself with the same function (same result).  Every load of a round
 // is issued before the first is used.
 template <int NORM>
-__device__ void stats_gather(const GemvArgs& a, int lane, float (*out)[3]) {
+__device__ void stats_gather(const GemvArgs& a, int lane, float (*out)[3], const WaveRows& wr) {
     constexpr int MAXR = 3 * DECODE_MAX_M;  // rows, at most
     const int need = 3 * a.M;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -219,7 +222,7 @@ __device__ void stats_gather(const GemvArgs& a, int lane, float (*out)[3]) {
     } else {
         for (int it = 0; it < need; ++it) {
             float K, S1, S2;
-            row_sums<NORM>(stats_row(a, it), a.d, lane, K, S1, S2);
+            row_sums<NORM>(stats_row(a, it, wr), a.d, lane, K, S1, S2);
             if (lane == 0) {
                 out[it][0] = K;
                 out[it][1] = S1;
@@ -273,13 +276,15 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
     // pairs, so the chunks of a column group tend to share an L2
     const int per = (nwg + 7) >> 3;
     const int lin = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    // every wave: the tokens' source rows and valid mask
+    const WaveRows wr = rv_wave(a.rv, M);
     // the statistics row of this workgroup id (if any): its start is loaded
     // first, so its latency overlaps the W' ring fill
     const bool producer = NORM != NORM_NONE && wave == 0 && (int)blockIdx.x < 3 * M;
     RowPre pre;
-    if (producer) row_preload(stats_row(a, blockIdx.x), d, lane, pre);
+    if (producer) row_preload(stats_row(a, blockIdx.x, wr), d, lane, pre);
     if (lin >= nwg) {
-        if (producer) stats_produce<NORM>(a, blockIdx.x, gridDim.x, lane, pre);
+        if (producer) stats_produce<NORM>(a, blockIdx.x, gridDim.x, lane, pre, wr);
         return;
     }
     const int grp = lin / nchunks, ch = lin - grp * nchunks;
@@ -290,6 +295,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
     const int NW = a.waves;
     const int nw = TC / NW;                // this wave's steps (a multiple of R)
     const uint16_t* __restrict__ hs = s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2]);
+    const size_t lds = (size_t)rv_ld(a.rv, s);
 
     // W' tiles of column block NB grp + b, k-step s T3 + tc0 + wave + NW i
     const u32x4* __restrict__ wp = reinterpret_cast<const u32x4*>(a.wp) +
@@ -301,7 +307,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
 #pragma unroll
     for (int tt = 0; tt < MT; ++tt) {
         const int m = min(16 * tt + (lane >> 2), M - 1);
-        ap[tt] = hs + (size_t)m * d + (size_t)(tc0 + wave) * 32 + 8 * coal_chunk(lane);
+        ap[tt] = hs + (size_t)rv_lane_src(wr, m) * lds + (size_t)(tc0 + wave) * 32 + 8 * coal_chunk(lane);
     }
     const int ASTEP = NW * 32;
 
@@ -323,7 +329,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
         __builtin_amdgcn_sched_barrier(0);
     }
     // statistics rows of this workgroup id, while the ring fills
-    if (producer) stats_produce<NORM>(a, blockIdx.x, gridDim.x, lane, pre);
+    if (producer) stats_produce<NORM>(a, blockIdx.x, gridDim.x, lane, pre, wr);
 
     // LDS: during the loop the waves' A transpose tiles, afterwards the
     // pairwise-reduction buffers, then the row-major tile
@@ -417,7 +423,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
     // published long before), so their loads share the round trip of the
     // partial stores and the last arriver does not wait for them.
     __shared__ float sh_row[3 * DECODE_MAX_M][3];  // (K, S1, S2) of row s M + m
-    if (NORM != NORM_NONE && wave == 0) stats_gather<NORM>(a, lane, sh_row);
+    if (NORM != NORM_NONE && wave == 0) stats_gather<NORM>(a, lane, sh_row, wr);
 
     // Publish: every wave waits until its coherent stores have completed
     // (the workgroup barrier alone does not wait for them), then thread 0
@@ -497,8 +503,8 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
                         y[e] += (NORM == NORM_NONE) ? pv : r * pv;
                     }
                 }
-                const uint2 w = make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
-                *reinterpret_cast<uint2*>(a.out + (size_t)m * d + n) = w;
+                const uint2 w = rv_ok(wr, m) ? make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])) : make_uint2(0u, 0u);
+                *reinterpret_cast<uint2*>(a.out + (size_t)m * (size_t)a.rv.ld_out + n) = w;
             }
         }
     }
@@ -544,17 +550,21 @@ __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
 #pragma unroll
     for (int p = 0; p < R; ++p) rw[p] = __builtin_nontemporal_load(&wp[(size_t)p * WSTEP]);
 
-    // token rows into LDS, states concatenated (row m: k = 0 .. 3d-1)
+    // token rows into LDS, states concatenated (row m: k = 0 .. 3d-1): the
+    // token's source row of each state
+    static_assert(WH_MAXM == 1, "the staging below reads one token's rows");
+    const WaveRows wr = rv_wave(a.rv, M);
     {
-        const uint64_t hp0 = reinterpret_cast<uint64_t>(a.h[0]);
-        const uint64_t hd1 = reinterpret_cast<uint64_t>(a.h[1]) - hp0;
-        const uint64_t hd2 = reinterpret_cast<uint64_t>(a.h[2]) - hp0;
+        const size_t srow = (size_t)rv_lane_src(wr, 0);
+        const uint64_t r0 = reinterpret_cast<uint64_t>(a.h[0] + srow * (size_t)a.rv.ld[0]);
+        const uint64_t rd1 = reinterpret_cast<uint64_t>(a.h[1] + srow * (size_t)a.rv.ld[1]) - r0;
+        const uint64_t rd2 = reinterpret_cast<uint64_t>(a.h[2] + srow * (size_t)a.rv.ld[2]) - r0;
         const int cpr = (3 * d) >> 3, cps = d >> 3;  // 16-byte chunks per row / per state
         for (int v = tid; v < M * cpr; v += 64 * WH_WAVES) {
             const int m = v / cpr, c = v - m * cpr;
             const int st = (c >= cps) + (c >= 2 * cps);
-            const uint64_t base = hp0 + (uint64_t)(st == 1) * hd1 + (uint64_t)(st == 2) * hd2;
-            const uint16_t* src = reinterpret_cast<const uint16_t*>(base) + (size_t)m * d + 8 * (c - st * cps);
+            const uint64_t base = r0 + (uint64_t)(st == 1) * rd1 + (uint64_t)(st == 2) * rd2;
+            const uint16_t* src = reinterpret_cast<const uint16_t*>(base) + 8 * (c - st * cps);
             *reinterpret_cast<uint4*>(la + m * rstride + c * 16) = *reinterpret_cast<const uint4*>(src);
         }
     }
@@ -662,7 +672,7 @@ __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
             if (NORM == NORM_LN) pv -= mu * a.u[(size_t)q * d + n];
             y += (NORM == NORM_NONE) ? pv : r * pv;
         }
-        a.out[(size_t)m * d + n] = (uint16_t)(pack_bf2(y, 0.f) & 0xffffu);
+        a.out[(size_t)m * (size_t)a.rv.ld_out + n] = rv_ok(wr, m) ? (uint16_t)(pack_bf2(y, 0.f) & 0xffffu) : (uint16_t)0;
     }
 }
 

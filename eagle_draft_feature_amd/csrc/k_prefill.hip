@@ -70,9 +70,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(
 // exchanges inside each quad of lanes (cb = 4 k + t; partners t ^ 1, then
 // t ^ 2) leave lane t with one row, row0 + (((t & 1) << 1) | (t >> 1)), and
 // the quad's 4 columns col0 + 4 k .. + 3: one 8-byte store, no staging
-// through LDS.  Rows from M and columns from d on are not stored.
-__device__ __forceinline__ void store_block_bf16(uint16_t* out, int M, int d, int row0, int col0, int cb, float v0,
-                                                 float v1, float v2, float v3) {
+// through LDS.  Rows from M and columns from d on are not stored; output
+// rows are ldo elements apart; row row0 + e is stored as zeros unless bit e
+// of okbits is set.
+__device__ __forceinline__ void store_block_bf16(uint16_t* out, int M, int d, long long ldo, int row0, int col0,
+                                                 int cb, uint32_t okbits, float v0, float v1, float v2, float v3) {
     const int t = cb & 3, k4 = cb >> 2;
     const bool odd = (t & 1) != 0, hi = t >= 2;
     auto swap1 = [](float x) {
@@ -85,10 +87,11 @@ __device__ __forceinline__ void store_block_bf16(uint16_t* out, int M, int d, in
     const uint32_t P1 = odd ? pack_bf2(r1, v3) : pack_bf2(v1, r1);
     // then each lane keeps one row of the quad's four columns
     const uint32_t rv = swap2(hi ? P0 : P1);
-    const uint2 w = hi ? make_uint2(rv, P1) : make_uint2(P0, rv);
-    const int m = row0 + (((t & 1) << 1) | (t >> 1));
+    const int e = ((t & 1) << 1) | (t >> 1);
+    const uint2 w = ((okbits >> e) & 1u) ? (hi ? make_uint2(rv, P1) : make_uint2(P0, rv)) : make_uint2(0u, 0u);
+    const int m = row0 + e;
     const int n = col0 + 4 * k4;
-    if (m < M && n < d) *reinterpret_cast<uint2*>(out + (size_t)m * d + n) = w;
+    if (m < M && n < d) *reinterpret_cast<uint2*>(out + (size_t)m * (size_t)ldo + n) = w;
 }
 
 struct TileCoord {
@@ -122,9 +125,10 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
     __shared__ __attribute__((aligned(1024))) char st1[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st2[STAGE_BYTES];
     __shared__ __attribute__((aligned(1024))) char st3[STAGE_BYTES];
-    // per-row factors of the tile: mu_0, rstd_0/rstd_1, mu_1, rstd_1/rstd_2, mu_2, rstd_2
+    // per-row factors of the tile: mu_0, rstd_0/rstd_1, mu_1, rstd_1/rstd_2, mu_2, rstd_2,
+    // then 1 / 0 for a token whose output row is stored / zeroed;
     // per-column factors: u_0, u_1, u_2, c
-    __shared__ float rowf[6][PBM];
+    __shared__ float rowf[7][PBM];
     __shared__ float colf[4][PBN];
     // end of a sub-step: the stage of sub-tile u + 2 has landed, i.e. all but
     // the newest 2 stages of loads (8 per wave each) are complete
@@ -151,27 +155,40 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
     //  A block ab: rows 16 ab + lane / 4, LDS chunk lane % 4 holds global
     //  chunk (lane % 4) ^ ((row / 4) % 4); rows past M re-read row M - 1.
     //  B tile bt: column block n0 / 16 + bt (clamped), k-step u.
-    // Addresses are a wave-uniform base plus a 32-bit per-lane byte offset.
+    // Addresses are a wave-uniform base plus a 32-bit per-lane byte offset:
+    // for A, the lane's source row times the state's row pitch (rows relative
+    // to the tile's first without an index list, absolute with one) plus its
+    // chunk.
     const int T = 3 * KTS;  // tiles per column block
     const int nblk = d >> 4;
-    uint32_t aoff[4];
+    const bool indexed = a.rv.idx != nullptr;
+    uint32_t arow[4], acol[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int r = 16 * (4 * wave + q) + (lane >> 2);
         const int c = (lane & 3) ^ ((r >> 2) & 3);
-        aoff[q] = (uint32_t)((min(m0 + r, M - 1) - m0) * d + 8 * c) * 2u;  // < 512 d bytes
+        const int m = min(m0 + r, M - 1);
+        bool ok;
+        arow[q] = indexed ? (uint32_t)rv_src(a.rv, m, ok) : (uint32_t)(m - m0);
+        acol[q] = (uint32_t)(16 * c);
     }
     const char* wbase = reinterpret_cast<const char*>(a.wt);
     const uint32_t boff = (uint32_t)lane * 16u;
+    auto a_state = [&](int u) __attribute__((always_inline)) { return u >= 2 * KTS ? 2 : (u >= KTS ? 1 : 0); };
     auto a_src = [&](int u) __attribute__((always_inline)) {
-        const int s = u >= 2 * KTS ? 2 : (u >= KTS ? 1 : 0);
-        return reinterpret_cast<const char*>((s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2])) + (size_t)m0 * d +
+        const int s = a_state(u);
+        const size_t first = indexed ? 0 : (size_t)m0 * (size_t)rv_ld(a.rv, s);
+        return reinterpret_cast<const char*>((s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2])) + first +
                                              (u * PBK - s * d));
     };
-    // load c (< 8) of the wave's share of sub-tile u into stage sa; hs = a_src(u)
-    auto issue_one = [&](int u, const char* hs, char* sa, int c) __attribute__((always_inline)) {
+    // row pitch of sub-tile u's state in bytes (the host keeps the offsets below 2^32)
+    auto a_pitch = [&](int u) __attribute__((always_inline)) {
+        return (uint32_t)__builtin_amdgcn_readfirstlane((int)(rv_ld(a.rv, a_state(u)) * 2));
+    };
+    // load c (< 8) of the wave's share of sub-tile u into stage sa; hs = a_src(u), ap = a_pitch(u)
+    auto issue_one = [&](int u, const char* hs, uint32_t ap, char* sa, int c) __attribute__((always_inline)) {
         if (c < 4) {
-            dma16(hs, aoff[c], lds_addr(sa + (4 * wave + c) * 1024));
+            dma16(hs, arow[c] * ap + acol[c], lds_addr(sa + (4 * wave + c) * 1024));
         } else {
             const int bt = 4 * wave + (c - 4);
             const int nb = min((n0 >> 4) + bt, nblk - 1);
@@ -193,6 +210,9 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
 
     if (tid < PBM) {
         const int m = m0 + tid;
+        bool tok_ok = false;
+        if (m < M) (void)rv_src(a.rv, m, tok_ok);
+        rowf[6][tid] = tok_ok ? 1.f : 0.f;
         float r[3] = {1.f, 1.f, 1.f}, mu[3] = {0.f, 0.f, 0.f};
         if (m < M && NORM != NORM_NONE) {
 #pragma unroll
@@ -275,9 +295,10 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
         __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
         const int un = min(u + 4, lim - 1);
         const char* hs = a_src(un);
+        const uint32_t ap = a_pitch(un);
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
-            if ((c & 1) == 0) issue_one(un, hs, cur, c >> 1);
+            if ((c & 1) == 0) issue_one(un, hs, ap, cur, c >> 1);
             read_one(nxt, set ^ 1, c);
             const int i = c >> 1;
 #pragma unroll
@@ -304,8 +325,9 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
             for (int v = 0; v < 4; ++v) {
                 const int uv = min(ua + v, lim - 1);
                 const char* hs = a_src(uv);
+                const uint32_t ap = a_pitch(uv);
 #pragma unroll
-                for (int c = 0; c < 8; ++c) issue_one(uv, hs, stv[v], c);
+                for (int c = 0; c < 8; ++c) issue_one(uv, hs, ap, stv[v], c);
                 __builtin_amdgcn_sched_barrier(0);
             }
             // stages 0 and 1 have landed; F(ua) from stage 0
@@ -356,9 +378,11 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         float r2[4], rm[3][4];
+        uint32_t okbits = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int rr = wm * 128 + 16 * i + 4 * g + e;
+            okbits |= rowf[6][rr] > 0.5f ? (1u << e) : 0u;
             r2[e] = NORM != NORM_NONE ? rowf[2][rr] : 1.f;
 #pragma unroll
             for (int q = 0; q < 3; ++q) rm[q][e] = NORM == NORM_LN ? rowf[3 + q][rr] : 0.f;
@@ -370,8 +394,8 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
         };
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            store_block_bf16(a.out, M, d, m0 + wm * 128 + 16 * i + 4 * g, n0 + wn * 128 + 16 * j, cb,
-                             fin(acc[i][j][0], j, 0), fin(acc[i][j][1], j, 1), fin(acc[i][j][2], j, 2),
+            store_block_bf16(a.out, M, d, a.rv.ld_out, m0 + wm * 128 + 16 * i + 4 * g, n0 + wn * 128 + 16 * j, cb,
+                             okbits, fin(acc[i][j][0], j, 0), fin(acc[i][j][1], j, 1), fin(acc[i][j][2], j, 2),
                              fin(acc[i][j][3], j, 3));
     }
 }
@@ -415,9 +439,13 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillArgs a, int 
 #pragma unroll
         for (int ss = 0; ss < 3; ++ss) uc[ss] = a.u[(size_t)ss * d + col];
     float y[4];
+    uint32_t okbits = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int m = min(row0 + e, M - 1);
+        bool ok;
+        (void)rv_src(a.rv, m, ok);
+        okbits |= ok ? (1u << e) : 0u;
         float acc = cn;
 #pragma unroll
         for (int ss = 0; ss < 3; ++ss) {
@@ -427,7 +455,7 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillArgs a, int 
         }
         y[e] = acc;
     }
-    store_block_bf16(a.out, M, d, row0, nt * PBN + wn * 128 + 16 * j, cb, y[0], y[1], y[2], y[3]);
+    store_block_bf16(a.out, M, d, a.rv.ld_out, row0, nt * PBN + wn * 128 + 16 * j, cb, okbits, y[0], y[1], y[2], y[3]);
 }
 
 PrefillPlan plan_prefill(int M, int d) {

@@ -7,6 +7,59 @@
 
 namespace e31 {
 
+// ---------------------------------------------------------------- row view
+// Where a call's rows are.  Token m reads row src(m) of each state s, at
+// h[s] + src(m) * ld[s] (elements), with src(m) = idx[m] when an index list
+// is given, else m; its output row is at out + m * ld_out.  An index outside
+// [0, n_src) reads row 0 instead, and that token's output row is written as
+// zeros.
+struct RowView {
+    long long ld[3] = {0, 0, 0};
+    long long ld_out = 0;
+    const int32_t* idx = nullptr;  // [M] (device) or null
+    int n_src = 0;                 // rows of each state buffer an index may name
+};
+inline RowView dense_rows(int M, int d) {
+    RowView v;
+    v.ld[0] = v.ld[1] = v.ld[2] = d;
+    v.ld_out = d;
+    v.n_src = M;
+    return v;
+}
+// leading dimension of state s (selects, no dynamic indexing of the argument)
+__device__ __forceinline__ long long rv_ld(const RowView& v, int s) {
+    return s == 0 ? v.ld[0] : (s == 1 ? v.ld[1] : v.ld[2]);
+}
+// source row of token m and whether it is valid (row 0 when it is not)
+__device__ __forceinline__ int rv_src(const RowView& v, int m, bool& ok) {
+    if (v.idx == nullptr) {
+        ok = true;
+        return m;
+    }
+    const int r = v.idx[m];
+    ok = r >= 0 && r < v.n_src;
+    return ok ? r : 0;
+}
+// For calls of at most 64 tokens, per wave: lane m holds token m's source
+// row (0 from M on), and a mask of the valid tokens.
+struct WaveRows {
+    int src;
+    uint64_t ok;
+};
+__device__ __forceinline__ WaveRows rv_wave(const RowView& v, int M) {
+    const int lane = threadIdx.x & 63;
+    bool ok = false;
+    int src = 0;
+    if (lane < M) src = rv_src(v, lane, ok);
+    WaveRows w;
+    w.src = src;
+    w.ok = __ballot(ok);
+    return w;
+}
+// token m's source row (m < 64, any lane)
+__device__ __forceinline__ int rv_lane_src(const WaveRows& w, int m) { return __shfl(w.src, m, 64); }
+__device__ __forceinline__ bool rv_ok(const WaveRows& w, int m) { return ((w.ok >> m) & 1ull) != 0; }
+
 // ---------------------------------------------------------------- row stats
 // Post-norm feedback rows (out = norm(x) * gamma + beta, one row per wave).
 constexpr int NORM_ROWS_MAX_D = 8192;
@@ -18,8 +71,8 @@ constexpr int EMBED_CONCAT_MAX_D = 8192;
 hipError_t launch_embed_concat(const int32_t* tokens, int M, int d, int vocab, const uint16_t* embed,
                                const uint16_t* fused, uint16_t* dst, int32_t* bad_count, hipStream_t st);
 
-hipError_t launch_row_stats(const uint16_t* h0, const uint16_t* h1, const uint16_t* h2, int M, int d, int norm,
-                            float eps, float* mu, float* rstd, hipStream_t st);
+hipError_t launch_row_stats(const uint16_t* h0, const uint16_t* h1, const uint16_t* h2, const RowView& rv, int M,
+                            int d, int norm, float eps, float* mu, float* rstd, hipStream_t st);
 
 // ------------------------------------------------------------------- decode
 // Small-M path on the stored W: one launch, split-K over W in its [3d, d]
@@ -30,7 +83,8 @@ struct DecodeArgs {
     const uint16_t* beta[3];   // NULL entry: beta = 0
     const uint16_t* W;         // [3d, d] (stored layout)
     const uint16_t* bias;      // [d] or NULL
-    uint16_t* out;             // [M, d]
+    uint16_t* out;             // [M, d] (rows at rv.ld_out)
+    RowView rv;
     int M, d;
     float eps;
     int nb;    // column blocks (16*J columns each)
@@ -71,7 +125,8 @@ struct GemvArgs {
     const uint16_t* wp;   // folded weight tiles
     const float* u;       // [3, d]
     const float* c;       // [d]
-    uint16_t* out;        // [M, d]
+    uint16_t* out;        // [M, d] (rows at rv.ld_out)
+    RowView rv;
     int M, d;
     float eps;
     int kps;              // K chunks per state (from the plan)
@@ -109,7 +164,8 @@ struct PrefillArgs {
     const float* c;       // [d]
     const float* mu;      // [3, M]
     const float* rstd;    // [3, M]
-    uint16_t* out;        // [M, d]
+    uint16_t* out;        // [M, d] (rows at rv.ld_out)
+    RowView rv;
     int M, d;
     int norm;
     int splits;           // 1 or a multiple of 3

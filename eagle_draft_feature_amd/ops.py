@@ -2,7 +2,9 @@
 
 torch provides device memory and the current HIP stream; nothing here
 computes.  All tensors must be contiguous bfloat16 (statistics and folded
-vectors float32) on the same GPU.
+vectors float32) on the same GPU, except the hidden states and output of
+fuse_rows / fuse_folded_rows: 2-D views whose rows may be any number of
+elements apart (unit column stride).
 """
 
 from __future__ import annotations
@@ -166,6 +168,78 @@ def fuse_folded(h_low, h_mid, h_high, norm, eps, w_folded: torch.Tensor, u: torc
     return out
 
 
+def _rows_view(t: torch.Tensor, name: str, d: Optional[int] = None, device=None):
+    """A [rows, d] bf16 view with unit column stride; returns its row stride."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be torch.bfloat16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D view with unit column stride")
+    if d is not None and t.shape[1] != d:
+        raise ValueError(f"{name} has {t.shape[1]} columns, expected {d}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t.stride(0) if t.shape[0] > 1 else max(t.shape[1], t.stride(0))
+
+
+def _row_args(h_low, h_mid, h_high, row_index, out):
+    import ctypes
+    d = h_low.shape[1] if h_low.dim() == 2 else -1
+    ld = [_rows_view(t, nm, d, h_low.device) for nm, t in (("h_low", h_low), ("h_mid", h_mid), ("h_high", h_high))]
+    n_src = h_low.shape[0]
+    if h_mid.shape[0] != n_src or h_high.shape[0] != n_src:
+        raise ValueError("the three states must hold the same number of rows")
+    dev = h_low.device
+    if row_index is not None:
+        _want(row_index, "row_index", dtype=torch.int32, device=dev)
+        if row_index.dim() != 1:
+            raise ValueError("row_index must be 1-D")
+        M = row_index.shape[0]
+    else:
+        M = n_src
+    if out is None:
+        out = torch.empty((M, d), dtype=torch.bfloat16, device=dev)
+    ld_out = _rows_view(out, "out", d, dev)
+    if out.shape[0] != M:
+        raise ValueError(f"out has {out.shape[0]} rows, expected {M}")
+    return M, d, dev, (ctypes.c_int64 * 3)(*ld), n_src, out, ld_out
+
+
+def fuse_rows(h_low, h_mid, h_high, norm, eps, gammas, betas, W: torch.Tensor, bias: Optional[torch.Tensor],
+              row_index: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """eagle31_fuse_rows: as fuse(), token m reading row row_index[m] (or m)
+    of the state views, which (like out) may have any row stride."""
+    M, d, dev, ld, n_src, out, ld_out = _row_args(h_low, h_mid, h_high, row_index, out)
+    _want(W, "W", shape=(3 * d, d), device=dev)
+    if bias is not None:
+        _want(bias, "bias", shape=(d,), device=dev)
+    g = _vec3(gammas, "gammas", d, dev)
+    b = _vec3(betas, "betas", d, dev)
+    st = lib().eagle31_fuse_rows(_ptr(h_low), _ptr(h_mid), _ptr(h_high), ld, _ptr(row_index), n_src, M, d,
+                                 norm_kind(norm), float(eps), g[0] if g else None, b[0] if b else None, _ptr(W),
+                                 _ptr(bias), _ptr(out), ld_out, _stream(h_low))
+    check("eagle31_fuse_rows", st)
+    return out
+
+
+def fuse_folded_rows(h_low, h_mid, h_high, norm, eps, w_folded: torch.Tensor, u: torch.Tensor, c: torch.Tensor,
+                     row_index: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """eagle31_fuse_folded_rows: as fuse_folded(), token m reading row
+    row_index[m] (or m) of the state views; any row strides."""
+    M, d, dev, ld, n_src, out, ld_out = _row_args(h_low, h_mid, h_high, row_index, out)
+    _want(w_folded, "w_folded", shape=folded_shape(d), device=dev)
+    _want(u, "u", dtype=torch.float32, shape=(3, d), device=dev)
+    _want(c, "c", dtype=torch.float32, shape=(d,), device=dev)
+    st = lib().eagle31_fuse_folded_rows(_ptr(h_low), _ptr(h_mid), _ptr(h_high), ld, _ptr(row_index), n_src, M, d,
+                                        norm_kind(norm), float(eps), _ptr(w_folded), _ptr(u), _ptr(c), _ptr(out),
+                                        ld_out, _stream(h_low))
+    check("eagle31_fuse_folded_rows", st)
+    return out
+
+
 def fuse_folded_noalloc(h_low, h_mid, h_high, norm, eps, w_folded: torch.Tensor, u: torch.Tensor, c: torch.Tensor,
                         out: torch.Tensor) -> torch.Tensor:
     """eagle31_fuse_folded_noalloc: the folded step on the library's fixed
@@ -219,7 +293,8 @@ def norm_output(x, norm, eps, gamma=None, beta=None, out=None):
 def embed_concat(tokens, embed, fused, out=None, bad_count=None):
     """eagle31_embed_concat: [embed[tokens[m]] | fused[m]] per row -> bf16
     [M, 2d].  tokens int32 [M]; bad_count: optional int32 [1] device tensor
-    that counts token ids outside the table (the caller zeroes it)."""
+    that counts token ids outside the table (the caller zeroes it).  With
+    fused None only the embedding half of out is written (out required)."""
     if (not isinstance(tokens, torch.Tensor) or tokens.dtype != torch.int32 or tokens.dim() != 1 or not tokens.is_cuda
             or not tokens.is_contiguous()):
         raise TypeError("tokens must be a contiguous 1-d int32 tensor on a GPU")
@@ -228,14 +303,17 @@ def embed_concat(tokens, embed, fused, out=None, bad_count=None):
         raise ValueError("embed must be [vocab, d]")
     vocab, d = embed.shape
     M = tokens.shape[0]
-    _want(fused, "fused", shape=(M, d), device=tokens.device)
+    if fused is not None:
+        _want(fused, "fused", shape=(M, d), device=tokens.device)
+    elif out is None:
+        raise ValueError("without fused, out must be given (its right half is left as it is)")
     if out is None:
         out = torch.empty((M, 2 * d), dtype=torch.bfloat16, device=tokens.device)
     _want(out, "out", shape=(M, 2 * d), device=tokens.device)
     if bad_count is not None and (bad_count.dtype != torch.int32 or bad_count.numel() != 1 or not bad_count.is_cuda):
         raise TypeError("bad_count must be a one-element int32 tensor on a GPU")
     st = lib().eagle31_embed_concat(_ptr(tokens), M, d, vocab, _ptr(embed), _ptr(fused), _ptr(out), _ptr(bad_count),
-                                    _stream(fused))
+                                    _stream(out))
     check("eagle31_embed_concat", st)
     return out
 

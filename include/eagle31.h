@@ -158,6 +158,50 @@ int eagle31_fuse_folded_ws(const void* h_low, const void* h_mid, const void* h_h
                            const float* c, void* out, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * eagle31_fuse_rows, eagle31_fuse_folded_rows - eagle31_fuse and
+ * eagle31_fuse_folded reading the hidden states where they already are and
+ * writing into a wider buffer, with no copy on either side (the vLLM EAGLE 3.1
+ * release post, devlery.com/blog/vllm-eagle31-attention-drift, section
+ * "vLLM main에 들어갔다는 것이 뉴스입니다": no hard-coded assumption about
+ * the target's hidden-state buffers):
+ *
+ *   token m (0 <= m < M) reads row src(m) of each state, at h_s + src(m) * ld[s]
+ *   elements, where src(m) = row_index[m] when row_index is given, else m;
+ *   its output row goes to out + m * ld_out.
+ *
+ * ld:        host int64[3]: elements between consecutive rows of h_low, h_mid,
+ *            h_high, each in [d, 2^22] and a multiple of 8 (NULL: d each).  The
+ *            states may be column blocks of one buffer, e.g. [n, 3d] with
+ *            h_mid = h_low + d, h_high = h_low + 2d and ld = 3d each.
+ * row_index: device int32 [M] or NULL, e.g. the positions of the accepted
+ *            tokens; any order, repeats allowed.  An index outside [0, n_src)
+ *            reads row 0 instead and that token's output row is written as
+ *            zeros (never a fault).
+ * n_src:     rows each state buffer holds, 1 <= n_src <= 2^31 - 1; at least M
+ *            without an index list.  With one, n_src * ld[s] * 2 bytes must not
+ *            exceed 2^32 for any state.
+ * out:       bf16, row m at out + m * ld_out, ld_out in [d, 2^22] and a
+ *            multiple of 8; e.g. the right half of the drafter-input buffer
+ *            [M, 2d] (out = dst + d, ld_out = 2d).  Only d values per row are
+ *            written.
+ * h_s and out 16-byte aligned, row_index 4-byte aligned.  out's extent
+ * ((M - 1) ld_out + d elements) must not overlap any state's
+ * ((n_src - 1) ld[s] + d), the index list or the weight-side arguments
+ * (EAGLE31_ERR_ALIAS).  Violations of the limits above: EAGLE31_ERR_SHAPE.
+ * Everything else (norm, weights, library-owned scratch, M == 0) as
+ * eagle31_fuse / eagle31_fuse_folded, whose results these equal bit for bit
+ * on the gathered rows.
+ */
+int eagle31_fuse_rows(const void* h_low, const void* h_mid, const void* h_high, const int64_t* ld,
+                      const int32_t* row_index, int64_t n_src, int64_t M, int64_t d, int norm_kind, float eps,
+                      const void* const* gamma, const void* const* beta, const void* W, const void* bias, void* out,
+                      int64_t ld_out, void* stream);
+int eagle31_fuse_folded_rows(const void* h_low, const void* h_mid, const void* h_high, const int64_t* ld,
+                             const int32_t* row_index, int64_t n_src, int64_t M, int64_t d, int norm_kind, float eps,
+                             const void* w_folded, const float* u, const float* c, void* out, int64_t ld_out,
+                             void* stream);
+
+/*
  * eagle31_fuse_folded_noalloc - eagle31_fuse_folded for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): the scratch memory (split-K partials,
@@ -218,11 +262,14 @@ int eagle31_norm_output(const void* x, int64_t M, int64_t d, int norm_kind, floa
  * honbul.tistory.com/173, section "EAGLE-3가 바꾼 것 2"):
  *
  *     dst[m, 0:d]  = embed[tokens[m], :]       (zeros if tokens[m] < 0 or >= vocab)
- *     dst[m, d:2d] = fused[m, :]
+ *     dst[m, d:2d] = fused[m, :]               (left untouched when fused is NULL)
  *
+ * With fused NULL only the embedding half is written: the fused feature can
+ * be written into dst[:, d:2d] directly by eagle31_fuse_rows /
+ * eagle31_fuse_folded_rows (out = dst + d, ld_out = 2d), with no copy.
  * tokens:    int32 [M], device, 4-byte aligned.
  * embed:     bf16 [vocab, d] row-major; fused: bf16 [M, d] (e.g. the output of
- *            eagle31_fuse); dst: bf16 [M, 2d]; all 16-byte aligned.
+ *            eagle31_fuse) or NULL; dst: bf16 [M, 2d]; all 16-byte aligned.
  * bad_count: device int32 or NULL; incremented once per token outside the
  *            table (the caller zeroes it).  Such a token never faults.
  * Bits are copied, nothing is rounded.  dst must not overlap any input.

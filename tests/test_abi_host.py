@@ -195,7 +195,9 @@ def _ecat(tok=0x700000, M=64, d=4096, vocab=16, e=WP, f=H1, dst=OUT, bad=None):
     (dict(M=-1), _capi.ERR_SHAPE),
     (dict(tok=None), _capi.ERR_NULL),
     (dict(e=None), _capi.ERR_NULL),
-    (dict(f=None), _capi.ERR_NULL),
+    (dict(f=None, e=None), _capi.ERR_NULL),   # fused may be NULL (embedding half only), embed may not
+    (dict(f=None, e=WP + 8), _capi.ERR_ALIGN),
+    (dict(f=H1 + 4), _capi.ERR_ALIGN),
     (dict(dst=None), _capi.ERR_NULL),
     (dict(tok=0x700002), _capi.ERR_ALIGN),
     (dict(bad=0x700001), _capi.ERR_ALIGN),
@@ -288,3 +290,67 @@ def test_verify_chunking_rules():
     assert _chunking(1, 0, 10)[0] == _capi.ERR_SHAPE
     assert _chunking(1, 1, (1 << 26) + 1)[0] == _capi.ERR_SHAPE
     assert e31.lib().eagle31_verify_chunking(1, 1, 10, None, ctypes.byref(ctypes.c_int32())) == _capi.ERR_NULL
+
+
+# strided / indexed rows: fake device addresses; d=128, states 16 MiB apart, out and index elsewhere
+RH0, RH1, RH2, ROUT, RIDX, RWF, RU, RC = 0x10000000, 0x11000000, 0x12000000, 0x13000000, 0x14000000, 0x15000000, \
+    0x16000000, 0x17000000
+
+
+def _frows(**kw):
+    a = dict(h0=RH0, h1=RH1, h2=RH2, ld=(128, 128, 128), idx=None, n_src=64, M=16, d=128, norm=1, eps=1e-5,
+             out=ROUT, ld_out=128, wf=RWF, u=RU, c=RC)
+    a.update(kw)
+    ld = None if a["ld"] is None else (ctypes.c_int64 * 3)(*a["ld"])
+    return e31.lib().eagle31_fuse_folded_rows(a["h0"], a["h1"], a["h2"], ld, a["idx"], a["n_src"], a["M"], a["d"],
+                                              a["norm"], a["eps"], a["wf"], a["u"], a["c"], a["out"], a["ld_out"],
+                                              None)
+
+
+def _srows(**kw):
+    a = dict(h0=RH0, h1=RH1, h2=RH2, ld=(128, 128, 128), idx=None, n_src=64, M=16, d=128, W=RWF, out=ROUT,
+             ld_out=128)
+    a.update(kw)
+    ld = None if a["ld"] is None else (ctypes.c_int64 * 3)(*a["ld"])
+    return e31.lib().eagle31_fuse_rows(a["h0"], a["h1"], a["h2"], ld, a["idx"], a["n_src"], a["M"], a["d"], 1, 1e-5,
+                                       None, None, a["W"], None, a["out"], a["ld_out"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ld=(120, 128, 128)), _capi.ERR_SHAPE),          # below d
+    (dict(ld=(128, 132, 128)), _capi.ERR_SHAPE),          # not a multiple of 8
+    (dict(ld=(128, 128, (1 << 22) + 8)), _capi.ERR_SHAPE),
+    (dict(ld_out=64), _capi.ERR_SHAPE),
+    (dict(ld_out=136 + 4), _capi.ERR_SHAPE),
+    (dict(n_src=0), _capi.ERR_SHAPE),
+    (dict(n_src=15), _capi.ERR_SHAPE),                    # fewer rows than tokens, no index list
+    (dict(n_src=2 ** 31), _capi.ERR_SHAPE),
+    (dict(idx=RIDX, n_src=(1 << 22) // 2 + 1, ld=(1 << 11, 128, 128)), _capi.ERR_SHAPE),  # > 4 GiB reachable
+    (dict(M=-1), _capi.ERR_SHAPE),
+    (dict(d=100), _capi.ERR_SHAPE),
+    (dict(norm=5), _capi.ERR_NORM_KIND),
+    (dict(h1=None), _capi.ERR_NULL),
+    (dict(out=None), _capi.ERR_NULL),
+    (dict(wf=None), _capi.ERR_NULL),
+    (dict(h2=RH2 + 8), _capi.ERR_ALIGN),
+    (dict(out=ROUT + 2), _capi.ERR_ALIGN),
+    (dict(idx=RIDX + 2), _capi.ERR_ALIGN),
+    (dict(out=RH0 + 63 * 256 * 2), _capi.ERR_ALIAS),   # inside h_low's last row at ld = 256
+    (dict(out=RIDX - 16 * 128 * 2 + 64, idx=RIDX), _capi.ERR_ALIAS),  # runs into the index list
+    (dict(out=RWF - 1024), _capi.ERR_ALIAS),           # runs into the folded weight
+    (dict(M=0, h0=None, out=None), _capi.OK),
+])
+def test_fuse_folded_rows_rejects_bad_arguments(kw, code):
+    if kw.get("out") == RH0 + 63 * 256 * 2:
+        kw = dict(kw, ld=(256, 128, 128))
+    assert _frows(**kw) == code
+
+
+def test_fuse_rows_strided_extent_checks():
+    # out 1 KiB past h_low's start: overlaps once h_low rows are 1024 elements apart
+    assert _srows(out=RH0 + 64 * 128 * 2 + 1024, ld=(1024, 128, 128)) == _capi.ERR_ALIAS
+    assert _srows(ld=(128, 128, 100)) == _capi.ERR_SHAPE
+    assert _srows(W=None) == _capi.ERR_NULL
+    assert _srows(idx=RIDX + 1) == _capi.ERR_ALIGN
+    # out rows 2d apart reach ((M - 1) * 2d + d) elements: into h0 when h0 starts there
+    assert _srows(out=RH0 - 15 * 256 * 2, ld_out=256) == _capi.ERR_ALIAS
