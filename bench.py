@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--no-prefill", action="store_true", help="skip the prefill measurements")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle timing on the host")
     p.add_argument("--only", choices=["decode", "decode_folded", "prefill", "rowstats", "copy", "postnorm", "postnorm_decode",
-                                             "embedcat", "verify"], default=None,
+                                             "embedcat", "verify", "rows"], default=None,
                    help="run a single leg (used under rocprofv3)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     return p.parse_args()
@@ -251,6 +251,73 @@ def prefill_leg(torch, pkg, synth, cfg, M, kind, eps, steps, warmup, folded=Fals
     return res
 
 
+def rows_leg(torch, pkg, synth, cfg, M, n_src, kind, eps, steps, warmup, mode):
+    """eagle31_fuse_folded_rows against the dense eagle31_fuse_folded on one
+    workload: `dense` reads three contiguous [M, d] states into [M, d];
+    `strided` reads them as column blocks of one [M, 3d] buffer and writes the
+    right half of an [M, 2d] drafter-input buffer; `indexed` gathers M rows
+    (seeded, any order, repeats) of an [n_src, 3d] buffer into the same
+    half-buffer.  Cold-cache rotation of every buffer and of W'; the bytes are
+    the folded step's (plus the index list)."""
+    import numpy as np
+    inp = synth.make_inputs(cfg, n_src if mode == "indexed" else M)
+    d = inp.d
+    rows = inp.M
+    foot = 3 * d * d * 2 + 3 * rows * d * 2 + 2 * M * d * 2
+    R = 2 if foot >= MALL_BYTES else rotation_count(foot)
+    base_W = to_dev(inp.W)
+    gamma = [to_dev(x) for x in inp.gamma]
+    beta = None if inp.beta is None else [to_dev(x) for x in inp.beta]
+    bias = None if inp.bias is None else to_dev(inp.bias)
+    idx = None
+    if mode == "indexed":
+        idx = torch.from_numpy(np.random.default_rng(M).integers(0, n_src, size=M).astype(np.int32)).to("cuda")
+    sets = []
+    for r in range(R):
+        wf, u, c = pkg.fold_prepare(kind, gamma, beta, base_W if r == 0 else base_W.clone(), bias)
+        if mode == "dense":
+            h = [to_dev(x) for x in inp.h]
+            out = torch.empty((M, d), dtype=torch.bfloat16, device="cuda")
+        else:
+            buf = torch.empty((rows, 3 * d), dtype=torch.bfloat16, device="cuda")
+            for k in range(3):
+                buf[:, k * d:(k + 1) * d] = to_dev(inp.h[k])
+            h = [buf[:, k * d:(k + 1) * d] for k in range(3)]
+            out = torch.empty((M, 2 * d), dtype=torch.bfloat16, device="cuda")[:, d:]
+        sets.append((h, (wf, u, c), out))
+    del base_W
+    torch.cuda.empty_cache()
+
+    def fn(i):
+        h, (wf, u, c), out = sets[i]
+        if mode == "dense":
+            pkg.fuse_folded(h[0], h[1], h[2], kind, eps, wf, u, c, out)
+        else:
+            pkg.fuse_folded_rows(h[0], h[1], h[2], kind, eps, wf, u, c, row_index=idx, out=out)
+
+    times = []
+    for _ in range(3):
+        t, _ = time_loop(torch, fn, R, steps, warmup)
+        times.append(t / steps)
+    per = statistics.median(times)
+    nbytes = folded_bytes(d, M) + (M * 4 if idx is not None else 0)
+    res = dict(mode=mode, workload=synth.CONFIGS[cfg].name, d=d, M=M, n_src=rows, R=R, steps=steps,
+               us_per_call=round(per * 1e6, 3), us_p10=round(min(times) * 1e6, 3), us_p90=round(max(times) * 1e6, 3),
+               hbm_frac=round(nbytes / per / 1e9 / HBM_PEAK_GBS, 4),
+               mfma_frac=round(flops(d, M) / per / 1e12 / BF16_PEAK_TFLOPS, 4))
+    del sets
+    torch.cuda.empty_cache()
+    return res
+
+
+def rows_legs(torch, pkg, synth, prefill=True):
+    out = [rows_leg(torch, pkg, synth, 2, 64, 256, 1, 1e-5, 200, 20, mode) for mode in ("dense", "strided", "indexed")]
+    if prefill:
+        out += [rows_leg(torch, pkg, synth, 5, 4096, 4096, 1, 1e-5, 20, 5, mode)
+                for mode in ("dense", "strided", "indexed")]
+    return out
+
+
 def postnorm_leg(torch, pkg, synth, cfg, M, kind, eps, steps, warmup):
     """eagle31_norm_output (post-norm feedback) on one workload's hidden-state
     shape: x read once, out written once, gamma and beta read once per call;
@@ -419,6 +486,9 @@ def main():
     if args.only == "verify":
         print(json.dumps([verify_leg(torch, pkg, synth, V) for V in (32000, 128256, 151936)]))
         return
+    if args.only == "rows":
+        print(json.dumps(rows_legs(torch, pkg, synth)))
+        return
     if args.only == "embedcat":
         print(json.dumps([embedcat_leg(torch, pkg, synth, 64, 4096, max(50, args.steps), args.warmup),
                           embedcat_leg(torch, pkg, synth, 32768, 7168, 20, 5)]))
@@ -506,6 +576,9 @@ def main():
     # the verify / accept step over the vocabulary (a next step of the path)
     verify = [verify_leg(torch, pkg, synth, V) for V in (32000, 128256, 151936)]
 
+    # strided / indexed hidden-state inputs against the dense entry point
+    rows = rows_legs(torch, pkg, synth, prefill=not args.no_prefill)
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline_leg(dec["inp"], dec["kind"], dec["eps"], args.cpu_seconds)
@@ -536,6 +609,7 @@ def main():
         "postnorm": postnorm,
         "embed_concat": embedcat,
         "verify": verify,
+        "rows": rows,
     }
     print(json.dumps(line))
 
