@@ -145,7 +145,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
         const size_t lds = (size_t)rv_ld(a.rv, s);
 
         // ---- provisional shift per token row: mean of the piece's first 32 values
-        const size_t shift_src = (size_t)rv_lane_src(wr, (tid >> 2) & 63);  // (every lane, before the branch)
+        const size_t shift_src = (size_t)rv_lane_src(a.rv, wr, (tid >> 2) & 63);  // (every lane, before the branch)
         if (NORM == NORM_LN && tid < 4 * DECODE_MAX_M) {
             const int m = tid >> 2;
             if (m < M) {
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
             gmk[tt] = (NORM == NORM_LN && m == M) ? 0xffffffffu : 0u;
             bmk[tt] = (NORM == NORM_LN && m == M + 1) ? 0xffffffffu : 0u;
             shift[tt] = (NORM == NORM_LN && is_tok) ? sh_shift[m] : 0.f;
-            const size_t src = (size_t)rv_lane_src(wr, min(m, 63));
+            const size_t src = (size_t)rv_lane_src(a.rv, wr, min(m, 63));
             arow[tt] = hs + (is_tok ? src : 0) * lds - seg_k0 + 8 * g;
         }
 

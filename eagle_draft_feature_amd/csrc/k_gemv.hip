@@ -155,7 +155,7 @@ __device__ __forceinline__ void row_sums(const uint16_t* row, int d, int lane, f
 __device__ __forceinline__ const uint16_t* stats_row(const GemvArgs& a, int it, const WaveRows& wr) {
     const int s = it / a.M, m = it - s * a.M;
     const uint16_t* hs = s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2]);
-    return hs + (size_t)rv_lane_src(wr, m) * (size_t)rv_ld(a.rv, s);
+    return hs + (size_t)rv_lane_src(a.rv, wr, m) * (size_t)rv_ld(a.rv, s);
 }
 
 // Producer side (one wave): rows first, first + stride, ... of the 3M
@@ -307,7 +307,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
 #pragma unroll
     for (int tt = 0; tt < MT; ++tt) {
         const int m = min(16 * tt + (lane >> 2), M - 1);
-        ap[tt] = hs + (size_t)rv_lane_src(wr, m) * lds + (size_t)(tc0 + wave) * 32 + 8 * coal_chunk(lane);
+        ap[tt] = hs + (size_t)rv_lane_src(a.rv, wr, m) * lds + (size_t)(tc0 + wave) * 32 + 8 * coal_chunk(lane);
     }
     const int ASTEP = NW * 32;
 
@@ -555,7 +555,7 @@ __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
     static_assert(WH_MAXM == 1, "the staging below reads one token's rows");
     const WaveRows wr = rv_wave(a.rv, M);
     {
-        const size_t srow = (size_t)rv_lane_src(wr, 0);
+        const size_t srow = (size_t)rv_lane_src(a.rv, wr, 0);
         const uint64_t r0 = reinterpret_cast<uint64_t>(a.h[0] + srow * (size_t)a.rv.ld[0]);
         const uint64_t rd1 = reinterpret_cast<uint64_t>(a.h[1] + srow * (size_t)a.rv.ld[1]) - r0;
         const uint64_t rd2 = reinterpret_cast<uint64_t>(a.h[2] + srow * (size_t)a.rv.ld[2]) - r0;

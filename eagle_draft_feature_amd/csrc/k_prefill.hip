@@ -65,6 +65,14 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
+// x >= y ? a : b on the scalar unit (wave-uniform operands): a compare and a
+// select, where the compiler would otherwise branch or build a lookup table
+__device__ __forceinline__ uint64_t sel_ge(int x, int y, uint64_t a, uint64_t b) {
+    uint64_t r;
+    asm("s_cmp_ge_i32 %1, %2\n\ts_cselect_b64 %0, %3, %4" : "=s"(r) : "s"(x), "s"(y), "s"(a), "s"(b) : "scc");
+    return r;
+}
+
 // Stores one lane's part of a 16 x 16 fp32 block as bf16.  Lane (g, cb) holds
 // rows row0 + e (e < 4; row0 = block row + 4 g) of column col0 + cb.  Two
 // exchanges inside each quad of lanes (cb = 4 k + t; partners t ^ 1, then
@@ -88,7 +96,9 @@ __device__ __forceinline__ void store_block_bf16(uint16_t* out, int M, int d, lo
     // then each lane keeps one row of the quad's four columns
     const uint32_t rv = swap2(hi ? P0 : P1);
     const int e = ((t & 1) << 1) | (t >> 1);
-    const uint2 w = ((okbits >> e) & 1u) ? (hi ? make_uint2(rv, P1) : make_uint2(P0, rv)) : make_uint2(0u, 0u);
+    const uint32_t keep = 0u - ((okbits >> e) & 1u);  // all ones, or zero for a token stored as zeros
+    const uint2 w0 = hi ? make_uint2(rv, P1) : make_uint2(P0, rv);
+    const uint2 w = make_uint2(w0.x & keep, w0.y & keep);
     const int m = row0 + e;
     const int n = col0 + 4 * k4;
     if (m < M && n < d) *reinterpret_cast<uint2*>(out + (size_t)m * (size_t)ldo + n) = w;
@@ -117,7 +127,10 @@ __device__ __forceinline__ TileCoord map_tile(int bid, int TM, int TN, int split
     return tc;
 }
 
-template <bool SPLIT, int NORM>
+// ULD: the three states share one row pitch, so each lane's A offsets are
+// computed once (the same for every state); otherwise they are formed at each
+// load from the lane's source row and the pitch of the state being loaded.
+template <bool SPLIT, int NORM, bool ULD>
 __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, int TN) {
     // four stages in separate arrays: with static stage indices the compiler
     // can tell the LDS-DMA writes of one stage from the reads of another
@@ -171,24 +184,29 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
         bool ok;
         arow[q] = indexed ? (uint32_t)rv_src(a.rv, m, ok) : (uint32_t)(m - m0);
         acol[q] = (uint32_t)(16 * c);
+        if (ULD) acol[q] += arow[q] * (uint32_t)(a.rv.ld[0] * 2);  // the whole offset, once
     }
     const char* wbase = reinterpret_cast<const char*>(a.wt);
     const uint32_t boff = (uint32_t)lane * 16u;
+    // per-state A bases (the tile's first row, or row 0 with an index list),
+    // each less its state's first k, so that sub-tile u of state s starts at
+    // base_s + 64 u bytes: two compare-and-selects, no branches
+    const uint64_t hb0 = (uint64_t)(uintptr_t)(a.h[0] + (indexed ? 0 : (size_t)m0 * (size_t)a.rv.ld[0]));
+    const uint64_t hb1 = (uint64_t)(uintptr_t)(a.h[1] + (indexed ? 0 : (size_t)m0 * (size_t)a.rv.ld[1])) - (uint64_t)d * 2u;
+    const uint64_t hb2 = (uint64_t)(uintptr_t)(a.h[2] + (indexed ? 0 : (size_t)m0 * (size_t)a.rv.ld[2])) - (uint64_t)d * 4u;
     auto a_state = [&](int u) __attribute__((always_inline)) { return u >= 2 * KTS ? 2 : (u >= KTS ? 1 : 0); };
     auto a_src = [&](int u) __attribute__((always_inline)) {
-        const int s = a_state(u);
-        const size_t first = indexed ? 0 : (size_t)m0 * (size_t)rv_ld(a.rv, s);
-        return reinterpret_cast<const char*>((s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2])) + first +
-                                             (u * PBK - s * d));
+        const uint64_t b = sel_ge(u, 2 * KTS, hb2, sel_ge(u, KTS, hb1, hb0));
+        return reinterpret_cast<const char*>(b + (uint64_t)u * (PBK * 2));
     };
     // row pitch of sub-tile u's state in bytes (the host keeps the offsets below 2^32)
     auto a_pitch = [&](int u) __attribute__((always_inline)) {
-        return (uint32_t)__builtin_amdgcn_readfirstlane((int)(rv_ld(a.rv, a_state(u)) * 2));
+        return ULD ? 0u : (uint32_t)__builtin_amdgcn_readfirstlane((int)(rv_ld(a.rv, a_state(u)) * 2));
     };
     // load c (< 8) of the wave's share of sub-tile u into stage sa; hs = a_src(u), ap = a_pitch(u)
     auto issue_one = [&](int u, const char* hs, uint32_t ap, char* sa, int c) __attribute__((always_inline)) {
         if (c < 4) {
-            dma16(hs, arow[c] * ap + acol[c], lds_addr(sa + (4 * wave + c) * 1024));
+            dma16(hs, ULD ? acol[c] : arow[c] * ap + acol[c], lds_addr(sa + (4 * wave + c) * 1024));
         } else {
             const int bt = 4 * wave + (c - 4);
             const int nb = min((n0 >> 4) + bt, nblk - 1);
@@ -479,7 +497,10 @@ template <bool SPLIT, int NORM>
 static hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& p, hipStream_t st) {
     const int items = p.tiles_m * p.tiles_n * (SPLIT ? p.splits : 1);
     const int grid = ((items + 7) / 8) * 8;
-    prefill_kernel<SPLIT, NORM><<<grid, PTH, 0, st>>>(a, p.tiles_m, p.tiles_n);
+    if (a.rv.ld[0] == a.rv.ld[1] && a.rv.ld[1] == a.rv.ld[2])
+        prefill_kernel<SPLIT, NORM, true><<<grid, PTH, 0, st>>>(a, p.tiles_m, p.tiles_n);
+    else
+        prefill_kernel<SPLIT, NORM, false><<<grid, PTH, 0, st>>>(a, p.tiles_m, p.tiles_n);
     if (SPLIT) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -56,8 +56,10 @@ __device__ __forceinline__ WaveRows rv_wave(const RowView& v, int M) {
     w.ok = __ballot(ok);
     return w;
 }
-// token m's source row (m < 64, any lane)
-__device__ __forceinline__ int rv_lane_src(const WaveRows& w, int m) { return __shfl(w.src, m, 64); }
+// token m's source row (m < 64, any lane); m itself without an index list
+__device__ __forceinline__ int rv_lane_src(const RowView& v, const WaveRows& w, int m) {
+    return v.idx == nullptr ? m : __shfl(w.src, m, 64);
+}
 __device__ __forceinline__ bool rv_ok(const WaveRows& w, int m) { return ((w.ok >> m) & 1ull) != 0; }
 
 // ---------------------------------------------------------------- row stats
