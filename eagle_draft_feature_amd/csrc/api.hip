@@ -113,7 +113,7 @@ int check_io(int64_t M, int64_t d, const void* h0, const void* h1, const void* h
 // ------------------------------------------------------------- workspace
 struct WsLayout {
     size_t counters = 0, counters_bytes = 0;
-    size_t stats = 0, part = 0, mu = 0, rstd = 0, wt = 0, u = 0, c = 0;
+    size_t stats = 0, part = 0, mu = 0, rstd = 0, wt = 0, u = 0, c = 0, cpart = 0;
     size_t total = 0;
 };
 
@@ -162,6 +162,8 @@ WsLayout layout_for(int64_t M, int64_t d, int norm, bool folded) {
         off += up256((size_t)3 * d * sizeof(float));
         L.c = off;
         off += up256((size_t)d * sizeof(float));
+        L.cpart = off;
+        off += up256((size_t)3 * d * sizeof(float));
     }
     L.total = off;
     return L;
@@ -351,7 +353,7 @@ int run_fuse(const Rows& R, int64_t M, int64_t d, int norm, float eps, const voi
         float* uw = at<float>(ws, L.u);
         float* cw = at<float>(ws, L.c);
         e = launch_fold_prepare((int)d, norm, g, b, static_cast<const uint16_t*>(W), static_cast<const uint16_t*>(bias),
-                                wtw, uw, cw, st);
+                                wtw, uw, cw, at<int>(ws, L.counters), at<float>(ws, L.cpart), st);
         if (e != hipSuccess) return hip_fail(e);
         wt = wtw;
         u = uw;
@@ -528,9 +530,16 @@ int eagle31_fold_prepare(int64_t d, int norm_kind, const void* const* gamma, con
         for (int s = 0; s < 3; ++s) g[s] = static_cast<const uint16_t*>(gamma[s]);
     if (norm_kind == NORM_LN && beta != nullptr)
         for (int s = 0; s < 3; ++s) b[s] = static_cast<const uint16_t*>(beta[s]);
+    // scratch: the strips' counters and the per-state partials of c
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    void* ws = nullptr;
+    size_t wsb = 0;
+    r = owned_workspace(COUNTER_REGION + up256((size_t)3 * d * sizeof(float)), st, &ws, &wsb);
+    if (r != EAGLE31_OK) return r;
     const hipError_t e = launch_fold_prepare((int)d, norm_kind, g, b, static_cast<const uint16_t*>(W),
                                              static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(w_folded), u,
-                                             c, static_cast<hipStream_t>(stream));
+                                             c, at<int>(ws, 0), at<float>(ws, COUNTER_REGION), st);
     if (e != hipSuccess) return hip_fail(e);
     return EAGLE31_OK;
 }

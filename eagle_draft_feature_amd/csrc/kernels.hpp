@@ -151,9 +151,10 @@ GemvPlan plan_gemv(int M, int d, int norm);
 hipError_t launch_gemv(const GemvArgs& a, int norm, const GemvPlan& p, hipStream_t st);
 
 // -------------------------------------------------------------- fold prepare
+// counters: [d / 64] zero on entry, left zero; cpart: [3, d] float32 scratch
 hipError_t launch_fold_prepare(int d, int norm, const uint16_t* const gamma[3], const uint16_t* const beta[3],
                                const uint16_t* W, const uint16_t* bias, uint16_t* wt, float* u, float* c,
-                               hipStream_t st);
+                               int* counters, float* cpart, hipStream_t st);
 
 // ------------------------------------------------------------------ prefill
 // Large-M path: GEMM on raw hidden states and the folded weight tiles,

@@ -137,7 +137,9 @@ int eagle31_fuse_ws(const void* h_low, const void* h_mid, const void* h_high, in
  *             (the beta term for LAYERNORM only).
  * Then, for the same norm_kind,
  *   out = sum_s rstd_s * (h_s . W'_s - mu_s * u_s) + c
- * equals eagle31_fuse's result up to rounding.
+ * equals eagle31_fuse's result up to rounding.  Uses a little library-owned
+ * scratch memory (3 d floats and d / 64 counters, per device and stream, as
+ * eagle31_fuse).  Deterministic.
  */
 int eagle31_fold_prepare(int64_t d, int norm_kind, const void* const* gamma, const void* const* beta,
                          const void* W, const void* bias, void* w_folded, float* u, float* c,
