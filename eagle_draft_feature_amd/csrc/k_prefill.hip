@@ -29,6 +29,8 @@
 // Few tiles (small M) split K by chunks that never cross a state; the chunks'
 // partials go to the workspace and a reduction kernel launched next on the
 // stream sums them in a fixed order and applies the statistics.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -483,10 +485,14 @@ PrefillPlan plan_prefill(int M, int d) {
     const int tiles = p.tiles_m * p.tiles_n;
     p.splits = 1;
     if (tiles < 192) {
-        // split K into chunks inside states until the grid covers the chip
-        int kps = 1;
+        // split K into chunks inside states: as many chunks per state as keep
+        // the grid within one round of the chip (one workgroup per CU).
+        // Measured at d=5120, M=128 / 256 and d=8192, M=512: a second round,
+        // or a part of one, costs more than the CUs it fills (the partials
+        // grow with the chunks); e.g. 4 chunks per state at d=5120, M=256 take
+        // 75 us where 8 take 94 us.
         const int KTS = d / PBK;
-        while (tiles * 3 * kps < 256 && kps * 2 <= KTS && kps < 8) kps *= 2;
+        const int kps = std::max(1, std::min(std::min(8, KTS), 256 / (3 * tiles)));
         p.splits = 3 * kps;
     }
     if (p.splits > 1) p.part_bytes = (size_t)tiles * p.splits * PTH * 64 * sizeof(f32x4);

@@ -101,7 +101,7 @@ def test_noalloc_allocates_nothing():
 
 
 def test_noalloc_refuses_too_large():
-    """d=8192, M=512 splits K over 6 chunks: ~96 MiB of partials, more than the
+    """d=8192, M=512 splits K over 3 chunks: 48 MiB of partials, more than the
     array holds; refused before any launch, and the next call is unaffected."""
     note("no-alloc too large")
     assert e31().noalloc_scratch_bytes() == 16 << 20
