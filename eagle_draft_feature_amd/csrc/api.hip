@@ -307,9 +307,10 @@ int run_fuse(const Rows& R, int64_t M, int64_t d, int norm, float eps, const voi
         a.waves = p.waves;
         a.counters = at<int>(ws, L.counters);
         a.part = at<float>(ws, L.part);
-        a.rstats = at<uint32_t>(ws, L.stats);
+        a.rstats = at<uint64_t>(ws, L.stats);
         a.call_id = next_call_id();
         a.stats_recompute = g_stats_recompute.load(std::memory_order_relaxed);
+        a.nch = p.nch;
         e = launch_gemv(a, norm, p, st);
         if (e != hipSuccess) return hip_fail(e);
         return EAGLE31_OK;

@@ -34,14 +34,19 @@
 // first 3M workgroups each reduce one (state, token) row of the hidden
 // states (one wave, coalesced 1 KiB loads; shifted sums S1 = sum (x - K),
 // S2 = sum (x - K)^2 with K the mean of the row's first 32 values, RMSNorm
-// sum x^2) and publish it; the workgroups that need the statistics (every
-// the last arriver of each column group) read them at their epilogue, long
-// after they were published.  The wait is bounded
-// (real-time clock): should it expire, the reader computes every row itself
-// with the same function, so the result is the same and every wave exits.
-// The handoff uses device-coherent stores and loads (see the split kernel):
-// a row's record carries the id of the call that wrote it, so stale records
-// of earlier calls are never mistaken for new ones and nothing is reset.
+// sum x^2) and publish it; the workgroups that need the statistics read them
+// after their main loop, long after they were published.  The wait is
+// bounded (real-time clock): should it expire, the reader computes every row
+// itself with the same function, so the result is the same and every wave
+// exits.  The handoff uses device-coherent stores and loads (see the split
+// kernel): each of a record's three values is one 64-bit word that carries
+// the id of the call that wrote it, so stale records of earlier calls are
+// never mistaken for new ones, nothing is reset, and the writer never waits.
+//
+// Two kernels share this: the column-split kernel (waves own column blocks,
+// chunks may cross states; the default from two tokens on where its grid
+// fills at least half the chip) and the split kernel (waves share a column
+// group's K chunk, chunks inside one state) for the other shapes.
 //
 // Token rows beyond M read row M-1 and are never stored.  Partial results
 // are combined in a fixed order: the output is bitwise reproducible.
@@ -158,10 +163,21 @@ __device__ __forceinline__ const uint16_t* stats_row(const GemvArgs& a, int it, 
     return hs + (size_t)rv_lane_src(a.rv, wr, m) * (size_t)rv_ld(a.rv, s);
 }
 
+// A statistics record: the three sums of a row, each published as one
+// 64-bit word (value bits, call id << 32) with a single atomic store, so
+// that a reader holding all three words with this call's id holds the
+// values, and the writer need not wait between stores.
+__device__ __forceinline__ void rec_store(uint64_t* p, float v, uint32_t id) {
+    __hip_atomic_store(p, (uint64_t)__float_as_uint(v) | ((uint64_t)id << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t rec_load(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Producer side (one wave): rows first, first + stride, ... of the 3M
-// (state, token) rows, published as the record (K, S1, S2, call id): the
-// three sums are stored first, then, once they have completed, the id.
-// `pre` holds the preloaded start of row `first` (if first < 3M).
+// (state, token) rows, each published as a record (K, S1, S2).  `pre` holds
+// the preloaded start of row `first` (if first < 3M).
 template <int NORM>
 __device__ void stats_produce(const GemvArgs& a, int first, int stride, int lane, const RowPre& pre,
                               const WaveRows& wr) {
@@ -171,12 +187,10 @@ __device__ void stats_produce(const GemvArgs& a, int first, int stride, int lane
         if (it == first) row_sums_pre<NORM>(stats_row(a, it, wr), a.d, lane, pre, K, S1, S2);
         else row_sums<NORM>(stats_row(a, it, wr), a.d, lane, K, S1, S2);
         if (lane == 0) {
-            uint32_t* rec = a.rstats + 4 * it;
-            store_coherent_u32(rec + 0, __float_as_uint(K));
-            store_coherent_u32(rec + 1, __float_as_uint(S1));
-            store_coherent_u32(rec + 2, __float_as_uint(S2));
-            __builtin_amdgcn_s_waitcnt(0);
-            store_coherent_u32(rec + 3, a.call_id);
+            uint64_t* rec = a.rstats + 4 * it;
+            rec_store(rec + 0, K, a.call_id);
+            rec_store(rec + 1, S1, a.call_id);
+            rec_store(rec + 2, S2, a.call_id);
         }
     }
 }
@@ -184,22 +198,28 @@ __device__ void stats_produce(const GemvArgs& a, int first, int stride, int lane
 // Reader side (one wave): all 3M rows into out[it][3] once every record
 // carries this call's id; waits at most about 200 us, then computes the
 // rows itself with the same function (same result).  Every load of a round
-// is issued before the first is used.
+// is issued before the first is used, and the round that finds every id
+// also holds the values.
 template <int NORM>
 __device__ void stats_gather(const GemvArgs& a, int lane, float (*out)[3], const WaveRows& wr) {
     constexpr int MAXR = 3 * DECODE_MAX_M;  // rows, at most
+    constexpr int J = MAXR / 64;           // rows per lane, at most
     const int need = 3 * a.M;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     bool ready = false;
+    uint64_t w[J][3];
     // (every load below is unconditional, its row clamped to the last one:
     // loads under a branch would each get a wait of their own)
     for (; !a.stats_recompute;) {
-        uint32_t f[MAXR / 64];
 #pragma unroll
-        for (int j = 0; j < MAXR / 64; ++j) f[j] = load_coherent_u32(a.rstats + 4 * min(lane + 64 * j, need - 1) + 3);
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int k = 0; k < 3; ++k) w[j][k] = rec_load(a.rstats + 4 * min(lane + 64 * j, need - 1) + k);
         bool mine = true;
 #pragma unroll
-        for (int j = 0; j < MAXR / 64; ++j) mine &= f[j] == a.call_id;
+        for (int j = 0; j < J; ++j)
+#pragma unroll
+            for (int k = 0; k < 3; ++k) mine &= (uint32_t)(w[j][k] >> 32) == a.call_id;
         if (__all(mine)) {
             ready = true;
             break;
@@ -208,16 +228,12 @@ __device__ void stats_gather(const GemvArgs& a, int lane, float (*out)[3], const
         __builtin_amdgcn_s_sleep(2);
     }
     if (ready) {
-        float v[3 * MAXR / 64];
 #pragma unroll
-        for (int j = 0; j < 3 * MAXR / 64; ++j) {
-            const int i = min(lane + 64 * j, 3 * need - 1), it = i / 3;
-            v[j] = __uint_as_float(load_coherent_u32(a.rstats + 4 * it + (i - 3 * it)));
-        }
+        for (int j = 0; j < J; ++j) {
+            const int it = lane + 64 * j;
+            if (it < need)
 #pragma unroll
-        for (int j = 0; j < 3 * MAXR / 64; ++j) {
-            const int i = lane + 64 * j;
-            if (i < 3 * need) (&out[0][0])[i] = v[j];
+                for (int k = 0; k < 3; ++k) out[it][k] = __uint_as_float((uint32_t)w[j][k]);
         }
     } else {
         for (int it = 0; it < need; ++it) {
@@ -676,6 +692,234 @@ __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
     }
 }
 
+// =====================================================================
+// Column split: one 16-column block per wave over a K chunk
+// =====================================================================
+//
+// Workgroup (group, chunk): NW waves, wave w owning column block NW group + w
+// over the chunk's k-steps, so no wave's result needs another's and the
+// workgroup ends without an LDS reduction.  The A tile of a k-step (MT
+// 16-row tiles, loaded coalesced as in the split kernel) is needed by every
+// wave, so it is loaded once per workgroup: in a group of NW k-steps wave w
+// loads k-step w's tiles into registers two groups ahead and writes them,
+// lane-linear, into one of two LDS stages one group ahead; one workgroup
+// barrier per group (LDS only) separates the writes of a stage from its
+// reads.  W' streams through a per-wave register ring RW k-steps deep.
+// Chunks need not align with the states: a chunk that crosses a state
+// boundary keeps the part before it in a second accumulator set.  The
+// chunk counts make the grid one workgroup per CU.  After its loop a
+// workgroup applies the statistics (gathered from the records the first 3M
+// workgroups published) to its part(s), so that a chunk leaves one summable
+// contribution, stored in fragment order (no re-layout); the last workgroup
+// of a column group to arrive adds c and the contributions in chunk order.
+constexpr int GN_RW = 8;     // W' ring: k-steps per wave
+constexpr int GN_MAXCH = 8;  // K chunks, at most
+
+template <int NORM, int MT, int NW>
+__global__ __launch_bounds__(64 * NW) void gemvn_kernel(GemvArgs a) {
+    constexpr int ATILE = MT * 1024;   // bytes of one k-step's A tiles
+    constexpr int GROUP = NW * ATILE;  // bytes of one group's (NW k-steps)
+    constexpr int BODY = GN_RW > 2 * NW ? GN_RW : 2 * NW;  // k-steps per unrolled body: even groups, whole ring
+    static_assert(BODY % GN_RW == 0 && BODY % (2 * NW) == 0, "ring and stages must be static in a body");
+    __shared__ __attribute__((aligned(16))) char sa[2][GROUP];
+    __shared__ float sh_row[3 * DECODE_MAX_M][3];
+    __shared__ int sh_last;
+    const int M = a.M, d = a.d;
+    const int TS = d >> 5, T = 3 * TS;
+    const int ngroups = d / (16 * NW), nch = a.nch, nwg = ngroups * nch;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, cb = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // XCD-aware order: each XCD takes a contiguous range of (group, chunk) pairs
+    const int per = (nwg + 7) >> 3;
+    const int lin = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    const WaveRows wr = rv_wave(a.rv, M);
+    const bool producer = NORM != NORM_NONE && wave == 0 && (int)blockIdx.x < 3 * M;
+    RowPre pre;
+    if (producer) row_preload(stats_row(a, blockIdx.x, wr), d, lane, pre);
+    if (lin >= nwg) {
+        if (producer) stats_produce<NORM>(a, blockIdx.x, gridDim.x, lane, pre, wr);
+        return;
+    }
+    const int grp = lin / nch, ch = lin - grp * nch;
+    const int t0 = (ch * T) / nch, nsteps = T / nch;  // the plan makes nsteps a multiple of BODY
+    const int s0 = t0 / TS;
+    const int tsplit = min(t0 + nsteps, (s0 + 1) * TS);  // first k-step of the next state (or the end)
+    const bool spans = tsplit < t0 + nsteps;
+    const int n = 16 * (NW * grp + wave) + cb;  // this lane's output column
+    const float us0 = NORM == NORM_LN && t0 == s0 * TS ? a.u[(size_t)s0 * d + n] : 0.f;
+    const float us1 = NORM == NORM_LN && spans ? a.u[(size_t)(s0 + 1) * d + n] : 0.f;
+
+    // A: this lane's row of each tile (clamped to M - 1) in the chunk's one or
+    // two states; element k of k-step t is at ap[state][tt] + 32 t
+    const uint16_t* ap0[MT];
+    const uint16_t* ap1[MT];
+    {
+        const int s1 = min(s0 + 1, 2);
+        const uint16_t* h0 = s0 == 0 ? a.h[0] : (s0 == 1 ? a.h[1] : a.h[2]);
+        const uint16_t* h1 = s1 == 0 ? a.h[0] : (s1 == 1 ? a.h[1] : a.h[2]);
+        const size_t ld0 = (size_t)rv_ld(a.rv, s0), ld1 = (size_t)rv_ld(a.rv, s1);
+#pragma unroll
+        for (int tt = 0; tt < MT; ++tt) {
+            const size_t src = (size_t)rv_lane_src(a.rv, wr, min(16 * tt + (lane >> 2), M - 1));
+            ap0[tt] = h0 + src * ld0 - (size_t)s0 * d + 8 * coal_chunk(lane);
+            ap1[tt] = h1 + src * ld1 - (size_t)s1 * d + 8 * coal_chunk(lane);
+        }
+    }
+    // k-step t's A tiles (the ones this lane loads)
+    auto aload = [&](int t, u32x4 (&x)[MT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int tt = 0; tt < MT; ++tt)
+            x[tt] = *reinterpret_cast<const u32x4*>((t < tsplit ? ap0[tt] : ap1[tt]) + (size_t)32 * t);
+    };
+    auto awrite = [&](int stage, const u32x4 (&x)[MT]) __attribute__((always_inline)) {
+        u32x4* dst = reinterpret_cast<u32x4*>(sa[stage] + wave * ATILE) + lane;
+#pragma unroll
+        for (int tt = 0; tt < MT; ++tt) dst[tt * 64] = x[tt];
+    };
+    const int ngrp = nsteps / NW;
+    const int fslot = frag_slot(lane);
+    // prologue: A of groups 0 and 1 first (their writes to the stages wait
+    // only for them: loads complete in issue order), then the W' ring, then
+    // group 2's A in flight
+    u32x4 ra[MT], rb[MT];
+    aload(t0 + wave, ra);
+    aload(t0 + NW + wave, rb);
+    // W' tiles of this wave's column block, k-steps t0 ..
+    const u32x4* __restrict__ wp = reinterpret_cast<const u32x4*>(a.wp) + ((size_t)(NW * grp + wave) * T + t0) * 64 + lane;
+    u32x4 rw[GN_RW];
+#pragma unroll
+    for (int p = 0; p < GN_RW; ++p) rw[p] = __builtin_nontemporal_load(wp + (size_t)min(p, nsteps - 1) * 64);
+    awrite(0, ra);
+    awrite(1, rb);
+    if (2 < ngrp) aload(t0 + 2 * NW + wave, ra);
+    __syncthreads();
+    // the statistics row of this workgroup id, from the row loaded at the
+    // start (the record needs no wait; the other waves run ahead to group 0's
+    // barrier meanwhile)
+    if (producer) stats_produce<NORM>(a, blockIdx.x, gridDim.x, lane, pre, wr);
+
+    f32x4 acc[MT], accs[MT];
+#pragma unroll
+    for (int tt = 0; tt < MT; ++tt) acc[tt] = accs[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b0 = 0; b0 < nsteps; b0 += BODY) {
+#pragma unroll
+        for (int gi = 0; gi < BODY / NW; ++gi) {
+            const int G = b0 / NW + gi;  // group index
+            const char* stg = sa[gi & 1];
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                const int i = G * NW + j;  // step inside the chunk
+                const int slot = (gi * NW + j) % GN_RW;
+                const u32x4 bw = rw[slot];
+                rw[slot] = __builtin_nontemporal_load(wp + (size_t)min(i + GN_RW, nsteps - 1) * 64);
+                u32x4 af[MT];
+#pragma unroll
+                for (int tt = 0; tt < MT; ++tt)
+                    af[tt] = *reinterpret_cast<const u32x4*>(stg + (j * MT + tt) * 1024 + fslot * 16);
+                if (t0 + i == tsplit) {
+#pragma unroll
+                    for (int tt = 0; tt < MT; ++tt) {
+                        accs[tt] = acc[tt];
+                        acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
+                }
+#pragma unroll
+                for (int tt = 0; tt < MT; ++tt) acc[tt] = mfma16x16x32(af[tt], bw, acc[tt]);
+            }
+            // every wave has read this stage: refill it with group G + 2
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+            if (G + 2 < ngrp) {
+                awrite(gi & 1, ra);
+                if (G + 3 < ngrp) aload(t0 + (G + 3) * NW + wave, ra);
+            }
+        }
+    }
+
+    // statistics: wave 0 gathers every row's record (published long before)
+    if (NORM != NORM_NONE && wave == 0) stats_gather<NORM>(a, lane, sh_row, wr);
+    __syncthreads();
+    // this wave's contribution of the chunk, sum over its state parts of
+    // rstd_s (P - mu_s u_s) (P for no norm), fragment order, stored at the
+    // device coherence point.  u_s sums the whole state, so mu_s u_s is
+    // subtracted once per state: by the part that starts at the state's
+    // first k-step (a part after a boundary always does).
+    const bool first0 = t0 == s0 * TS;
+    f32x4 y[MT];
+#pragma unroll
+    for (int tt = 0; tt < MT; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = min(16 * tt + 4 * g + e, M - 1);
+            float v = spans ? accs[tt][e] : acc[tt][e];
+            if (NORM != NORM_NONE) {
+                float mu, r;
+                const float st[3] = {sh_row[s0 * M + m][0], sh_row[s0 * M + m][1], sh_row[s0 * M + m][2]};
+                row_norm<NORM>(st, d, a.eps, mu, r);
+                v = r * (NORM == NORM_LN && first0 ? v - mu * us0 : v);
+            }
+            if (spans) {
+                float v1 = acc[tt][e];
+                if (NORM != NORM_NONE) {
+                    float mu, r;
+                    const int s1 = s0 + 1;
+                    const float st[3] = {sh_row[s1 * M + m][0], sh_row[s1 * M + m][1], sh_row[s1 * M + m][2]};
+                    row_norm<NORM>(st, d, a.eps, mu, r);
+                    v1 = r * (NORM == NORM_LN ? v1 - mu * us1 : v1);
+                }
+                v += v1;
+            }
+            y[tt][e] = v;
+        }
+    const size_t wtile = (size_t)MT * 64;  // f32x4 of one wave's part
+    auto part_base = [&](int c) { return a.part + (((size_t)grp * nch + c) * NW + wave) * wtile * 4; };
+    {
+        const __amdgpu_buffer_rsrc_t rs = part_rsrc(part_base(ch), (int)(wtile * 16));
+#pragma unroll
+        for (int tt = 0; tt < MT; ++tt) store_coherent16(rs, (tt * 64 + lane) * 16, __builtin_bit_cast(u32x4, y[tt]));
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const int old = __hip_atomic_fetch_add(a.counters + grp, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sh_last = (old == nch - 1);
+    }
+    __syncthreads();
+    if (!sh_last) return;
+
+    // ================= last arriver of column group grp =================
+    // wave w: column block NW grp + w; the chunks' contributions, all loads
+    // issued first, summed in chunk order
+    const float cn = a.c[n];
+    u32x4 v[GN_MAXCH][MT];
+#pragma unroll
+    for (int c = 0; c < GN_MAXCH; ++c)
+        if (c < nch) {
+            const __amdgpu_buffer_rsrc_t rs = part_rsrc(part_base(c), (int)(wtile * 16));
+#pragma unroll
+            for (int tt = 0; tt < MT; ++tt) v[c][tt] = load_coherent16(rs, (tt * 64 + lane) * 16);
+        }
+    f32x4 tot[MT];
+#pragma unroll
+    for (int tt = 0; tt < MT; ++tt) tot[tt] = f32x4{cn, cn, cn, cn};
+#pragma unroll
+    for (int c = 0; c < GN_MAXCH; ++c)
+        if (c < nch)
+#pragma unroll
+            for (int tt = 0; tt < MT; ++tt) tot[tt] += __builtin_bit_cast(f32x4, v[c][tt]);
+#pragma unroll
+    for (int tt = 0; tt < MT; ++tt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = 16 * tt + 4 * g + e;
+            if (m < M)
+                a.out[(size_t)m * (size_t)a.rv.ld_out + n] =
+                    rv_ok(wr, m) ? (uint16_t)(pack_bf2(tot[tt][e], 0.f) & 0xffffu) : (uint16_t)0;
+        }
+    if (tid == 0) __hip_atomic_store(a.counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ----------------------------------------------------------------- host side
 GemvPlan plan_gemv(int M, int d, int norm) {
     (void)norm;
@@ -698,6 +942,29 @@ GemvPlan plan_gemv(int M, int d, int norm) {
             p.grid = d / 16;
             p.counters_bytes = 256;
             p.part_bytes = 256;
+            return p;
+        }
+    }
+    // The column-split kernel: 8 waves (128 columns) per workgroup and the
+    // most K chunks that keep the grid at one workgroup per CU, each chunk a
+    // whole number of unrolled bodies (k-steps); at least 128 workgroups.
+    if (M >= 2) {
+        constexpr int NW = 8;
+        const int body = std::max(GN_RW, 2 * NW);
+        const int ngroups = d / (16 * NW);
+        int best = 0;
+        if (d % (16 * NW) == 0)
+            for (int nch = 1; nch <= GN_MAXCH && ngroups * nch <= 256; ++nch)
+                if (T3 * 3 % (nch * body) == 0) best = nch;
+        if (best > 0 && ngroups * best >= 128) {
+            p.cols = 1;
+            p.nch = best;
+            p.waves = NW;
+            p.nb = NW;
+            p.kps = 1;
+            p.grid = ngroups * best;
+            p.counters_bytes = ((size_t)ngroups * sizeof(int) + 255) / 256 * 256;
+            p.part_bytes = ((size_t)ngroups * best * NW * p.MT * 64 * 16 + 255) / 256 * 256;
             return p;
         }
     }
@@ -794,7 +1061,30 @@ static hipError_t launch_whole(const GemvArgs& a, const GemvPlan& p, hipStream_t
     return hipGetLastError();
 }
 
+template <int NORM>
+static hipError_t launch_cols(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
+    const int grid = ((p.grid + 7) / 8) * 8;
+    switch (p.MT) {
+        case 1: gemvn_kernel<NORM, 1, 8><<<grid, 512, 0, st>>>(a); break;
+        case 2: gemvn_kernel<NORM, 2, 8><<<grid, 512, 0, st>>>(a); break;
+        case 3: gemvn_kernel<NORM, 3, 8><<<grid, 512, 0, st>>>(a); break;
+        case 4: gemvn_kernel<NORM, 4, 8><<<grid, 512, 0, st>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv(const GemvArgs& a, int norm, const GemvPlan& p, hipStream_t st) {
+    if (p.cols) {
+        const int T = 3 * a.d / 32, body = std::max(GN_RW, 16);
+        if (p.waves != 8 || a.nch != p.nch || p.nch < 1 || p.nch > GN_MAXCH || a.d % 128 || T % (p.nch * body) ||
+            a.M < 2 || a.M > DECODE_MAX_M || (p.MT - 1) * 16 >= a.M || p.MT * 16 < a.M ||
+            (long long)(a.d / 128) * p.nch != p.grid)
+            return hipErrorInvalidValue;
+        if (norm == NORM_LN) return launch_cols<NORM_LN>(a, p, st);
+        if (norm == NORM_RMS) return launch_cols<NORM_RMS>(a, p, st);
+        return launch_cols<NORM_NONE>(a, p, st);
+    }
     if (p.whole) {
         if (a.M < 1 || a.M > WH_MAXM || a.M * (6 * a.d + 64) > WH_A_BYTES || a.d % (32 * WH_WAVES) ||
             p.grid != a.d / 16)

@@ -135,16 +135,19 @@ struct GemvArgs {
     int waves;            // waves per workgroup (from the plan)
     int* counters;        // [column groups], zero on entry, left zero on exit
     float* part;          // [column groups * 3 kps * 16 MT * 16 nb]
-    uint32_t* rstats;     // [3 M][4]: (K, S1, S2, call id) per (state, token) row
+    uint64_t* rstats;     // [3 M][4]: K, S1, S2 per (state, token) row, each (value bits | call id << 32)
     uint32_t call_id;     // nonzero, different from the previous calls' on this workspace
     int stats_recompute;  // nonzero: readers recompute the statistics instead of waiting for the records
+    int nch;              // column-split kernel: K chunks (from the plan)
 };
 
 struct GemvPlan {
     int kps = 0, ring = 0, waves = 0, nb = 4, MT = 1, grid = 0;  // nb: 16-column blocks per workgroup
     int whole = 0;  // 1: few tokens, the whole-K kernel (one 16-column block per workgroup, no split)
+    int cols = 0;   // 1: the column-split kernel (a 16-column block per wave, nch K chunks)
+    int nch = 0;
     size_t counters_bytes = 0, part_bytes = 0;
-    static constexpr size_t rstats_bytes = 3 * 64 * 4 * sizeof(uint32_t);
+    static constexpr size_t rstats_bytes = 3 * 64 * 4 * sizeof(uint64_t);
 };
 
 GemvPlan plan_gemv(int M, int d, int norm);
