@@ -64,7 +64,7 @@ def measured_traffic(M):
     since the counters were taken."""
     import hashlib
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                        "gemv_split_d4096_M64_layernorm.md")
+                        "gemv_cols_d4096_M64_layernorm.md")
     if M != 64 or not os.path.exists(path):
         return None
     rec = None
@@ -215,7 +215,7 @@ def decode_leg(torch, pkg, synth, M, steps, warmup, entry="folded", repeats=5):
     return res
 
 
-def prefill_leg(torch, pkg, synth, cfg, M, kind, eps, steps, warmup, folded=False):
+def prefill_leg(torch, pkg, synth, cfg, M, kind, eps, steps, warmup, folded=False, repeats=5):
     """One workload through eagle31_fuse (stored W) or eagle31_fuse_folded
     (weight folded beforehand), cold-cache rotation; reports tokens/s and the
     fraction of both peaks (HBM with the entry point's algorithmic bytes,
@@ -236,13 +236,16 @@ def prefill_leg(torch, pkg, synth, cfg, M, kind, eps, steps, warmup, folded=Fals
         else:
             pkg.fuse(h[0], h[1], h[2], kind, eps, rot.gamma, rot.beta, W, rot.bias, out)
 
-    t, _ = time_loop(torch, fn, R, steps, warmup)
-    per = t / steps
+    times = []
+    for _ in range(repeats):
+        t, _ = time_loop(torch, fn, R, steps, warmup)
+        times.append(t / steps)
+    per = statistics.median(times)
     nbytes = folded_bytes(inp.d, M) if folded else alg_bytes(inp.d, M, kind, inp.beta is not None,
                                                               inp.bias is not None)
     res = dict(workload=synth.CONFIGS[cfg].name, d=inp.d, M=M, norm=synth.workloads.NORM_NAMES[kind],
-               variant="folded" if folded else "plain", steps=steps,
-               ms_per_step=per * 1e3, tokens_per_s=M / per,
+               variant="folded" if folded else "plain", steps=steps, repeats=repeats,
+               ms_per_step=per * 1e3, ms_p10=min(times) * 1e3, ms_p90=max(times) * 1e3, tokens_per_s=M / per,
                hbm_frac=nbytes / per / 1e9 / HBM_PEAK_GBS,
                mfma_frac=flops(inp.d, M) / per / 1e12 / BF16_PEAK_TFLOPS,
                tflops=flops(inp.d, M) / per / 1e12)
@@ -416,7 +419,17 @@ def verify_leg(torch, pkg, synth, V, B=64, N=4, steps=100, warmup=10):
     return res
 
 
-def cpu_baseline_leg(inp, kind, eps, budget_s):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline_leg(inp, kind, eps, budget_s, what="the full decode batch"):
     """The fp64 oracle as it stands, on preconverted float64 arrays, repeated
     until about budget_s seconds of host work."""
     import numpy as np
@@ -440,8 +453,8 @@ def cpu_baseline_leg(inp, kind, eps, budget_s):
         el = time.perf_counter() - t0
         if el >= budget_s or n >= 10000:
             break
-    return dict(value=inp.M * n / el, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"{n} oracle calls of the full decode batch (d={inp.d}, M={inp.M}) on float64 "
+    return dict(value=inp.M * n / el, unit="tokens/s", cores=threads, kind="oracle", cpu_model=cpu_model(),
+                sample=f"{n} oracle calls of {what} (d={inp.d}, M={inp.M}) on float64 "
                        f"arrays, {el:.1f} s; BLAS threads {threads}")
 
 
@@ -481,7 +494,8 @@ def main():
         print(json.dumps(copy_leg(torch)))
         return
     if args.only == "prefill":
-        print(json.dumps(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, max(3, args.steps), args.warmup, folded=True)))
+        print(json.dumps(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, max(3, args.steps), args.warmup, folded=True,
+                                     repeats=1 if args.steps < 10 else 5)))
         return
     if args.only == "verify":
         print(json.dumps([verify_leg(torch, pkg, synth, V) for V in (32000, 128256, 151936)]))
@@ -528,7 +542,7 @@ def main():
     achieved = dec["bytes"] / (kern_us * 1e-6) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(args.M),
-                    kernel="gemv_split_kernel (eagle31_fuse_folded, 2<=M<=64)",
+                    kernel="gemvn_kernel (eagle31_fuse_folded, column split, 2<=M<=64)",
                     bytes_per_launch=dec["bytes"], launch_us_mean=round(kern_us, 3),
                     launch_us_mean_single_events=round(dec["event_us_mean"], 3))
 
@@ -547,8 +561,8 @@ def main():
     prefill = []
     others = []
     if not args.no_prefill:
-        prefill.append(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, 10, 3, folded=False))
-        prefill.append(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, 10, 3, folded=True))
+        prefill.append(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, 20, 3, folded=False))
+        prefill.append(prefill_leg(torch, pkg, synth, 4, 32768, 1, 1e-5, 20, 3, folded=True))
         prefill.append(prefill_leg(torch, pkg, synth, 5, 4096, 1, 1e-5, 30, 5, folded=False))
         prefill.append(prefill_leg(torch, pkg, synth, 5, 4096, 1, 1e-5, 30, 5, folded=True))
         # the other sizes of the draft-tree and chunked-prefill workloads
@@ -580,8 +594,14 @@ def main():
     rows = rows_legs(torch, pkg, synth, prefill=not args.no_prefill)
 
     cpu = None
+    cpu_prefill = None
     if not args.no_cpu:
         cpu = cpu_baseline_leg(dec["inp"], dec["kind"], dec["eps"], args.cpu_seconds)
+        if not args.no_prefill:
+            # a bounded sample of the long-context prefill workload: its first 512 rows
+            pf = cached_inputs(synth, 4, synth.CONFIGS[4].max_M).rows(512)
+            cpu_prefill = cpu_baseline_leg(pf, 1, 1e-5, args.cpu_seconds,
+                                           what="the first 512 rows of the long-context prefill workload")
 
     line = {
         "metric": METRIC,
@@ -603,6 +623,7 @@ def main():
                    "fold_prepare_us": round(dec["fold_prepare_us"], 1)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_baseline_prefill": cpu_prefill,
         "decode_sweep": sweep,
         "prefill": prefill,
         "other_workloads": others,
