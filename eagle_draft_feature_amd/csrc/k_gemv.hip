@@ -263,6 +263,50 @@ __device__ __forceinline__ void row_norm(const float (&st)[3], int d, float eps,
     }
 }
 
+// Reader side for one wave's share of the rows: row first + lane (below
+// 3M) as (mu, rstd) into out[row] once its record carries this call's id
+// (the same bounded wait and the same fallback as stats_gather, so the same
+// bits).  One round trip when the records are there.
+template <int NORM>
+__device__ void stats_gather_rows(const GemvArgs& a, int lane, int first, float (*out)[2], const WaveRows& wr) {
+    const int need = 3 * a.M;
+    const int it = min(first + lane, need - 1);
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    bool ready = false;
+    uint64_t w[3];
+    for (; !a.stats_recompute;) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) w[k] = rec_load(a.rstats + 4 * it + k);
+        bool mine = true;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) mine &= (uint32_t)(w[k] >> 32) == a.call_id;
+        if (__all(mine)) {
+            ready = true;
+            break;
+        }
+        if (__builtin_amdgcn_s_memrealtime() - t0 > 20000) break;  // 100 MHz clock
+        __builtin_amdgcn_s_sleep(2);
+    }
+    float st[3];
+    if (ready) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) st[k] = __uint_as_float((uint32_t)w[k]);
+    } else {
+        // the wave recomputes its rows one by one; lane r keeps row first + r
+        const int last = min(first + 64, need);
+        for (int r = first; r < last; ++r) {
+            float K, S1, S2;
+            row_sums<NORM>(stats_row(a, r, wr), a.d, lane, K, S1, S2);
+            if (r == it) {
+                st[0] = K;
+                st[1] = S1;
+                st[2] = S2;
+            }
+        }
+    }
+    if (first + lane < need) row_norm<NORM>(st, a.d, a.eps, out[it][0], out[it][1]);
+}
+
 // =====================================================================
 // 64 or 128 columns x one K chunk per workgroup
 // =====================================================================
@@ -455,6 +499,15 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
     if (!sh_last) return;
 
     // ================= last arriver of column group grp =================
+    // each row's (mu, rstd) once, from the gathered sums
+    __shared__ float sh_mr[3 * DECODE_MAX_M][2];
+    if (NORM != NORM_NONE) {
+        for (int it = tid; it < 3 * M; it += blockDim.x) {
+            const float st[3] = {sh_row[it][0], sh_row[it][1], sh_row[it][2]};
+            row_norm<NORM>(st, d, a.eps, sh_mr[it][0], sh_mr[it][1]);
+        }
+        __syncthreads();
+    }
     // outputs: thread -> 4 consecutive columns (c4), rows rg, rg + rstep, ...
     // Each pass covers 4 rows x 3 states x 2 chunks: its 24 16-byte loads are
     // all issued before the first is used.  Chunks are summed in their order.
@@ -509,8 +562,8 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
                 for (int ss = 0; ss < 3; ++ss) {
                     float mu = 0.f, r = 1.f;
                     if (NORM != NORM_NONE) {
-                        const float st[3] = {sh_row[ss * M + m][0], sh_row[ss * M + m][1], sh_row[ss * M + m][2]};
-                        row_norm<NORM>(st, d, a.eps, mu, r);
+                        mu = sh_mr[ss * M + m][0];
+                        r = sh_mr[ss * M + m][1];
                     }
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -722,7 +775,7 @@ __global__ __launch_bounds__(64 * NW) void gemvn_kernel(GemvArgs a) {
     constexpr int BODY = GN_RW > 2 * NW ? GN_RW : 2 * NW;  // k-steps per unrolled body: even groups, whole ring
     static_assert(BODY % GN_RW == 0 && BODY % (2 * NW) == 0, "ring and stages must be static in a body");
     __shared__ __attribute__((aligned(16))) char sa[2][GROUP];
-    __shared__ float sh_row[3 * DECODE_MAX_M][3];
+    __shared__ float sh_mr[3 * DECODE_MAX_M][2];  // (mu, rstd) of each (state, token) row
     __shared__ int sh_last;
     const int M = a.M, d = a.d;
     const int TS = d >> 5, T = 3 * TS;
@@ -837,8 +890,9 @@ __global__ __launch_bounds__(64 * NW) void gemvn_kernel(GemvArgs a) {
         }
     }
 
-    // statistics: wave 0 gathers every row's record (published long before)
-    if (NORM != NORM_NONE && wave == 0) stats_gather<NORM>(a, lane, sh_row, wr);
+    // statistics (published long before): wave w gathers rows 64 w ..
+    // 64 w + 63 and turns each row's sums into (mu, rstd) for the workgroup
+    if (NORM != NORM_NONE && 64 * wave < 3 * M) stats_gather_rows<NORM>(a, lane, 64 * wave, sh_mr, wr);
     __syncthreads();
     // this wave's contribution of the chunk, sum over its state parts of
     // rstd_s (P - mu_s u_s) (P for no norm), fragment order, stored at the
@@ -854,18 +908,14 @@ __global__ __launch_bounds__(64 * NW) void gemvn_kernel(GemvArgs a) {
             const int m = min(16 * tt + 4 * g + e, M - 1);
             float v = spans ? accs[tt][e] : acc[tt][e];
             if (NORM != NORM_NONE) {
-                float mu, r;
-                const float st[3] = {sh_row[s0 * M + m][0], sh_row[s0 * M + m][1], sh_row[s0 * M + m][2]};
-                row_norm<NORM>(st, d, a.eps, mu, r);
+                const float mu = sh_mr[s0 * M + m][0], r = sh_mr[s0 * M + m][1];
                 v = r * (NORM == NORM_LN && first0 ? v - mu * us0 : v);
             }
             if (spans) {
                 float v1 = acc[tt][e];
                 if (NORM != NORM_NONE) {
-                    float mu, r;
                     const int s1 = s0 + 1;
-                    const float st[3] = {sh_row[s1 * M + m][0], sh_row[s1 * M + m][1], sh_row[s1 * M + m][2]};
-                    row_norm<NORM>(st, d, a.eps, mu, r);
+                    const float mu = sh_mr[s1 * M + m][0], r = sh_mr[s1 * M + m][1];
                     v1 = r * (NORM == NORM_LN ? v1 - mu * us1 : v1);
                 }
                 v += v1;

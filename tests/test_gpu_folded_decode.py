@@ -100,6 +100,29 @@ def test_folded_decode_bitwise_over_many_calls():
     assert_parity(bf16_to_f64(refs[9]), oracle_out(inp.rows(9), LN, 1e-5), "folded M=9")
 
 
+@pytest.mark.parametrize("d,M,kind", [(3584, 64, LN), (3584, 17, NONE), (5120, 33, RMS), (8192, 2, LN),
+                                      (4096, 64, RMS)])
+def test_folded_decode_stats_fallback_same_bits_every_chunking(d, M, kind):
+    """The statistics readers' fallback (recompute the rows), forced from the
+    host, gives the same bits as the normal path at chunkings with 4, 6, 7 and
+    8 K chunks (d=3584: chunks that cross a state boundary, so a chunk's part
+    applies two states' statistics) and 1, 2, 3, 4 token tiles; both match
+    the oracle."""
+    eps = {LN: 1e-5, RMS: 1e-6, NONE: 0.0}[kind]
+    note(f"stats fallback d={d} M={M} kind={kind}")
+    w = synth.gen.custom_workload(d, (M,), seed_tag=d * 7 + M)
+    inp = synth.make_inputs(w, M)
+    dv = DevInputs(inp)
+    normal, prepared = folded_call(dv, kind, eps)
+    e31().debug_stats_recompute(True)
+    try:
+        forced, _ = folded_call(dv, kind, eps, prepared)
+    finally:
+        e31().debug_stats_recompute(False)
+    assert torch.equal(normal.view(torch.int16), forced.view(torch.int16)), "fallback differs"
+    assert_parity(bf16_to_f64(forced), oracle_out(inp, kind, eps), f"fallback d={d} M={M} kind={kind}")
+
+
 @pytest.mark.parametrize("M", [4, 64])
 def test_folded_decode_dc_offset(M):
     """A shared offset of 100 sigma on h_high through the folded path: the
