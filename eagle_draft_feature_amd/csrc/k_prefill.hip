@@ -12,18 +12,19 @@
 // adding c.  The statistics come from the row-statistics pass that runs
 // first.
 //
-// Tiling for gfx950: 256 x 256 output tile, BK = 64, 256 threads (4 waves
-// as 2 x 2, each wave 128 x 128 = 8 x 8 MFMA 16x16x32 blocks, whose 256
-// accumulator registers the compiler keeps in AGPRs).  Operands go from
-// global memory straight to LDS (16-byte LDS-DMA loads, no register
-// staging), double-buffered: the loads of k-tile t+1 are issued before the
-// MFMAs of k-tile t.  A (hidden states, row-major) lands 8 rows x 128 bytes
-// per wave load; its 16-byte chunks are XOR-swizzled by (row / 2) mod 8 on
-// the global side, so the 16 rows of a fragment read hit distinct banks.
-// W' arrives as 1 KiB MFMA B-fragment tiles (16 columns x 32 k, lane l's
-// operand at bytes [16 l, 16 l + 16)), copied to LDS as they are, so a B
-// operand is one conflict-free 16-byte read.  Tiles are walked in groups
-// of 4 M-tiles, and consecutive workgroup ids are spread so that each XCD
+// Tiling for gfx950: 256 x 256 output tile, 256 threads (4 waves as 2 x 2,
+// each wave 128 x 128 = 8 x 8 MFMA 16x16x32 blocks, whose 256 accumulator
+// registers the compiler keeps in AGPRs), k in sub-tiles of 32 (one MFMA
+// k-step) through four 32 KiB LDS stages.  Operands go from global memory
+// straight to LDS (16-byte LDS-DMA loads, no register staging).  A (hidden
+// states, row-major) lands as 16-row x 64-byte blocks, one per wave load;
+// its 16-byte chunks are XOR-swizzled by (row / 4) mod 4 on the global side,
+// so the 16 rows of a fragment read hit distinct banks.  W' arrives as 1 KiB
+// MFMA B-fragment tiles (16 columns x 32 k, lane l's operand at bytes
+// [16 l, 16 l + 16)), copied to LDS as they are, so a B operand is one
+// conflict-free 16-byte read.  Each sub-step issues the loads of the
+// sub-tile needed 2-3 sub-steps later.  Tiles are walked in groups of 4
+// M-tiles, and consecutive workgroup ids are spread so that each XCD
 // (workgroup id mod 8) takes a contiguous run of that order: the tiles an
 // XCD runs at once share A and B tiles in its L2.
 // Few tiles (small M) split K by chunks that never cross a state; the chunks'
