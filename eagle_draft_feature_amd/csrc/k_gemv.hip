@@ -86,6 +86,12 @@ __device__ __forceinline__ int frag_slot(int lane) {
     return 4 * r + (g ^ ((r >> 2) & 3));
 }
 
+// Two k-steps of a 16-row A tile as 128-byte row pieces: 16-byte chunk c
+// of row r sits in LDS slot 8 r + (c ^ pair_swz(r)), r the row's index in its
+// 16-row block.  The 16 rows of a fragment read then hit distinct banks
+// whether a 16-byte LDS access is served 8 or 16 lanes at a time.
+__device__ __forceinline__ int pair_swz(int r) { return (r ^ (r >> 3)) & 7; }
+
 // Shifted sums of one hidden-state row, by one wave: K = mean of the row's
 // first 32 values, S1 = sum (x - K), S2 = sum (x - K)^2 (RMSNorm: K = 0,
 // S2 = sum x^2).  Eight coalesced 1 KiB loads per pass; every lane returns
@@ -802,8 +808,14 @@ __global__ __launch_bounds__(64 * NW) void gemvn_kernel(GemvArgs a) {
     const float us0 = NORM == NORM_LN && t0 == s0 * TS ? a.u[(size_t)s0 * d + n] : 0.f;
     const float us1 = NORM == NORM_LN && spans ? a.u[(size_t)(s0 + 1) * d + n] : 0.f;
 
-    // A: this lane's row of each tile (clamped to M - 1) in the chunk's one or
-    // two states; element k of k-step t is at ap[state][tt] + 32 t
+    // A, by k-step pairs: in a group of NW k-steps wave w loads half
+    // w % 2 (rows 8 MT (w % 2) ..) of the 16 MT token rows of pair w / 2, as
+    // MT loads of 8 rows x 128 bytes (two k-steps), so that a load touches 8
+    // whole cache lines (16 rows x 64 bytes touch 16 and cost the load units
+    // about twice as much).  Load q of this lane: row 8 MT (w % 2) + 8 q +
+    // lane / 8 (clamped to M - 1), chunk (lane % 8) ^ pair_swz(row); element
+    // k of the pair starting at k-step t is at ap[state][q] + 32 t.  A pair
+    // never crosses a state: chunks and states start at even k-steps.
     const uint16_t* ap0[MT];
     const uint16_t* ap1[MT];
     {
@@ -812,31 +824,39 @@ __global__ __launch_bounds__(64 * NW) void gemvn_kernel(GemvArgs a) {
         const uint16_t* h1 = s1 == 0 ? a.h[0] : (s1 == 1 ? a.h[1] : a.h[2]);
         const size_t ld0 = (size_t)rv_ld(a.rv, s0), ld1 = (size_t)rv_ld(a.rv, s1);
 #pragma unroll
-        for (int tt = 0; tt < MT; ++tt) {
-            const size_t src = (size_t)rv_lane_src(a.rv, wr, min(16 * tt + (lane >> 2), M - 1));
-            ap0[tt] = h0 + src * ld0 - (size_t)s0 * d + 8 * coal_chunk(lane);
-            ap1[tt] = h1 + src * ld1 - (size_t)s1 * d + 8 * coal_chunk(lane);
+        for (int q = 0; q < MT; ++q) {
+            const int row = 8 * MT * (wave & 1) + 8 * q + (lane >> 3);
+            const int c = (lane & 7) ^ pair_swz(row & 15);
+            const size_t src = (size_t)rv_lane_src(a.rv, wr, min(row, M - 1));
+            ap0[q] = h0 + src * ld0 - (size_t)s0 * d + 8 * c;
+            ap1[q] = h1 + src * ld1 - (size_t)s1 * d + 8 * c;
         }
     }
-    // k-step t's A tiles (the ones this lane loads)
+    const int wpair = 2 * (wave >> 1);  // first k-step of this wave's pair in a group
+    // this lane's part of the pair starting at k-step t
     auto aload = [&](int t, u32x4 (&x)[MT]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int tt = 0; tt < MT; ++tt)
-            x[tt] = *reinterpret_cast<const u32x4*>((t < tsplit ? ap0[tt] : ap1[tt]) + (size_t)32 * t);
+        for (int q = 0; q < MT; ++q)
+            x[q] = *reinterpret_cast<const u32x4*>((t < tsplit ? ap0[q] : ap1[q]) + (size_t)32 * t);
     };
+    // stage layout: pair p (of the group's NW / 2) at p 2048 MT bytes, row r at
+    // + 128 r; each load lands 8 rows (1 KiB) contiguous
     auto awrite = [&](int stage, const u32x4 (&x)[MT]) __attribute__((always_inline)) {
-        u32x4* dst = reinterpret_cast<u32x4*>(sa[stage] + wave * ATILE) + lane;
+        char* dst = sa[stage] + (wave >> 1) * (2048 * MT) + (8 * MT * (wave & 1)) * 128 + lane * 16;
 #pragma unroll
-        for (int tt = 0; tt < MT; ++tt) dst[tt * 64] = x[tt];
+        for (int q = 0; q < MT; ++q) *reinterpret_cast<u32x4*>(dst + q * 1024) = x[q];
     };
     const int ngrp = nsteps / NW;
-    const int fslot = frag_slot(lane);
+    // fragment reads: row 16 tt + lane % 16, chunk lane / 16 of the pair's
+    // first (aread0) or second (aread1) k-step
+    const int aread0 = cb * 128 + 16 * (g ^ pair_swz(cb));
+    const int aread1 = cb * 128 + 16 * ((4 + g) ^ pair_swz(cb));
     // prologue: A of groups 0 and 1 first (their writes to the stages wait
     // only for them: loads complete in issue order), then the W' ring, then
     // group 2's A in flight
     u32x4 ra[MT], rb[MT];
-    aload(t0 + wave, ra);
-    aload(t0 + NW + wave, rb);
+    aload(t0 + wpair, ra);
+    aload(t0 + NW + wpair, rb);
     // W' tiles of this wave's column block, k-steps t0 ..
     const u32x4* __restrict__ wp = reinterpret_cast<const u32x4*>(a.wp) + ((size_t)(NW * grp + wave) * T + t0) * 64 + lane;
     u32x4 rw[GN_RW];
@@ -844,7 +864,7 @@ __global__ __launch_bounds__(64 * NW) void gemvn_kernel(GemvArgs a) {
     for (int p = 0; p < GN_RW; ++p) rw[p] = __builtin_nontemporal_load(wp + (size_t)min(p, nsteps - 1) * 64);
     awrite(0, ra);
     awrite(1, rb);
-    if (2 < ngrp) aload(t0 + 2 * NW + wave, ra);
+    if (2 < ngrp) aload(t0 + 2 * NW + wpair, ra);
     __syncthreads();
     // the statistics row of this workgroup id, from the row loaded at the
     // start (the record needs no wait; the other waves run ahead to group 0's
@@ -868,7 +888,8 @@ __global__ __launch_bounds__(64 * NW) void gemvn_kernel(GemvArgs a) {
                 u32x4 af[MT];
 #pragma unroll
                 for (int tt = 0; tt < MT; ++tt)
-                    af[tt] = *reinterpret_cast<const u32x4*>(stg + (j * MT + tt) * 1024 + fslot * 16);
+                    af[tt] = *reinterpret_cast<const u32x4*>(stg + (j >> 1) * (2048 * MT) + tt * 2048 +
+                                                             ((j & 1) ? aread1 : aread0));
                 if (t0 + i == tsplit) {
 #pragma unroll
                     for (int tt = 0; tt < MT; ++tt) {
@@ -885,7 +906,7 @@ __global__ __launch_bounds__(64 * NW) void gemvn_kernel(GemvArgs a) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
             if (G + 2 < ngrp) {
                 awrite(gi & 1, ra);
-                if (G + 3 < ngrp) aload(t0 + (G + 3) * NW + wave, ra);
+                if (G + 3 < ngrp) aload(t0 + (G + 3) * NW + wpair, ra);
             }
         }
     }
