@@ -124,13 +124,21 @@ size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 // rest) the previous call used.
 constexpr size_t COUNTER_REGION = 16384;  // 4096 counters
 constexpr int MAX_COUNTERS = (int)(COUNTER_REGION / sizeof(int));
+// The folded path takes the decode kernels up to 64 tokens, and the
+// column-split decode kernel up to 128 where its plan exists; more tokens
+// take the prefill kernel.
+bool folded_decode(int64_t M, int64_t d, int norm) {
+    if (M <= DECODE_MAX_M) return true;
+    return M <= GEMVN_MAX_M && plan_gemv((int)M, (int)d, norm).cols != 0;
+}
+
 WsLayout layout_for(int64_t M, int64_t d, int norm, bool folded) {
     WsLayout L;
     if (M <= 0) return L;
     L.counters = 0;
     L.counters_bytes = COUNTER_REGION;
     size_t off = COUNTER_REGION;
-    if (M <= DECODE_MAX_M && folded) {
+    if (folded && folded_decode(M, d, norm)) {
         const GemvPlan p = plan_gemv((int)M, (int)d, norm);
         L.stats = off;
         off += up256(GemvPlan::rstats_bytes);
@@ -290,7 +298,7 @@ int run_fuse(const Rows& R, int64_t M, int64_t d, int norm, float eps, const voi
         for (int s = 0; s < 3; ++s) b[s] = static_cast<const uint16_t*>(beta[s]);
 
     hipError_t e;
-    if (M <= DECODE_MAX_M && folded) {
+    if (folded && folded_decode(M, d, norm)) {
         const GemvPlan p = plan_gemv((int)M, (int)d, norm);
         if (p.waves == 0 || d / (16 * p.nb) > MAX_COUNTERS) return EAGLE31_ERR_SHAPE;
         GemvArgs a;

@@ -781,7 +781,7 @@ __global__ __launch_bounds__(64 * NW) void gemvn_kernel(GemvArgs a) {
     constexpr int BODY = GN_RW > 2 * NW ? GN_RW : 2 * NW;  // k-steps per unrolled body: even groups, whole ring
     static_assert(BODY % GN_RW == 0 && BODY % (2 * NW) == 0, "ring and stages must be static in a body");
     __shared__ __attribute__((aligned(16))) char sa[2][GROUP];
-    __shared__ float sh_mr[3 * DECODE_MAX_M][2];  // (mu, rstd) of each (state, token) row
+    __shared__ float sh_mr[3 * GEMVN_MAX_M][2];  // (mu, rstd) of each (state, token) row
     __shared__ int sh_last;
     const int M = a.M, d = a.d;
     const int TS = d >> 5, T = 3 * TS;
@@ -960,34 +960,41 @@ __global__ __launch_bounds__(64 * NW) void gemvn_kernel(GemvArgs a) {
     if (!sh_last) return;
 
     // ================= last arriver of column group grp =================
-    // wave w: column block NW grp + w; the chunks' contributions, all loads
-    // issued first, summed in chunk order
+    // wave w: column block NW grp + w; the chunks' contributions, summed in
+    // chunk order, in batches of up to 4 token tiles whose loads are all
+    // issued before the first is used (one round trip per batch)
     const float cn = a.c[n];
-    u32x4 v[GN_MAXCH][MT];
+    constexpr int TB = MT < 4 ? MT : 4;
 #pragma unroll
-    for (int c = 0; c < GN_MAXCH; ++c)
-        if (c < nch) {
-            const __amdgpu_buffer_rsrc_t rs = part_rsrc(part_base(c), (int)(wtile * 16));
+    for (int tb = 0; tb < MT; tb += TB) {
+        u32x4 v[GN_MAXCH][TB];
 #pragma unroll
-            for (int tt = 0; tt < MT; ++tt) v[c][tt] = load_coherent16(rs, (tt * 64 + lane) * 16);
-        }
-    f32x4 tot[MT];
+        for (int c = 0; c < GN_MAXCH; ++c)
+            if (c < nch) {
+                const __amdgpu_buffer_rsrc_t rs = part_rsrc(part_base(c), (int)(wtile * 16));
 #pragma unroll
-    for (int tt = 0; tt < MT; ++tt) tot[tt] = f32x4{cn, cn, cn, cn};
+                for (int k = 0; k < TB; ++k)
+                    if (tb + k < MT) v[c][k] = load_coherent16(rs, ((tb + k) * 64 + lane) * 16);
+            }
+        f32x4 tot[TB];
 #pragma unroll
-    for (int c = 0; c < GN_MAXCH; ++c)
-        if (c < nch)
+        for (int k = 0; k < TB; ++k) tot[k] = f32x4{cn, cn, cn, cn};
 #pragma unroll
-            for (int tt = 0; tt < MT; ++tt) tot[tt] += __builtin_bit_cast(f32x4, v[c][tt]);
+        for (int c = 0; c < GN_MAXCH; ++c)
+            if (c < nch)
 #pragma unroll
-    for (int tt = 0; tt < MT; ++tt)
+                for (int k = 0; k < TB; ++k)
+                    if (tb + k < MT) tot[k] += __builtin_bit_cast(f32x4, v[c][k]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int m = 16 * tt + 4 * g + e;
-            if (m < M)
-                a.out[(size_t)m * (size_t)a.rv.ld_out + n] =
-                    rv_ok(wr, m) ? (uint16_t)(pack_bf2(tot[tt][e], 0.f) & 0xffffu) : (uint16_t)0;
-        }
+        for (int k = 0; k < TB; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = 16 * (tb + k) + 4 * g + e;
+                if (tb + k < MT && m < M)
+                    a.out[(size_t)m * (size_t)a.rv.ld_out + n] =
+                        rv_ok(wr, m) ? (uint16_t)(pack_bf2(tot[k][e], 0.f) & 0xffffu) : (uint16_t)0;
+            }
+    }
     if (tid == 0) __hip_atomic_store(a.counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1019,7 +1026,7 @@ GemvPlan plan_gemv(int M, int d, int norm) {
     // The column-split kernel: 8 waves (128 columns) per workgroup and the
     // most K chunks that keep the grid at one workgroup per CU, each chunk a
     // whole number of unrolled bodies (k-steps); at least 128 workgroups.
-    if (M >= 2) {
+    if (M >= 2 && M <= GEMVN_MAX_M) {
         constexpr int NW = 8;
         const int body = std::max(GN_RW, 2 * NW);
         const int ngroups = d / (16 * NW);
@@ -1039,6 +1046,7 @@ GemvPlan plan_gemv(int M, int d, int norm) {
             return p;
         }
     }
+    if (M > DECODE_MAX_M) return GemvPlan{};  // more tokens: the column split or nothing (prefill)
     // Column blocks per workgroup: 8 (128 columns) from two token tiles on,
     // which halves how often the workgroups re-read the hidden states; the
     // wider tile then keeps fewer k-steps in flight (registers).
@@ -1140,6 +1148,10 @@ static hipError_t launch_cols(const GemvArgs& a, const GemvPlan& p, hipStream_t 
         case 2: gemvn_kernel<NORM, 2, 8><<<grid, 512, 0, st>>>(a); break;
         case 3: gemvn_kernel<NORM, 3, 8><<<grid, 512, 0, st>>>(a); break;
         case 4: gemvn_kernel<NORM, 4, 8><<<grid, 512, 0, st>>>(a); break;
+        case 5: gemvn_kernel<NORM, 5, 8><<<grid, 512, 0, st>>>(a); break;
+        case 6: gemvn_kernel<NORM, 6, 8><<<grid, 512, 0, st>>>(a); break;
+        case 7: gemvn_kernel<NORM, 7, 8><<<grid, 512, 0, st>>>(a); break;
+        case 8: gemvn_kernel<NORM, 8, 8><<<grid, 512, 0, st>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1149,7 +1161,7 @@ hipError_t launch_gemv(const GemvArgs& a, int norm, const GemvPlan& p, hipStream
     if (p.cols) {
         const int T = 3 * a.d / 32, body = std::max(GN_RW, 16);
         if (p.waves != 8 || a.nch != p.nch || p.nch < 1 || p.nch > GN_MAXCH || a.d % 128 || T % (p.nch * body) ||
-            a.M < 2 || a.M > DECODE_MAX_M || (p.MT - 1) * 16 >= a.M || p.MT * 16 < a.M ||
+            a.M < 2 || a.M > GEMVN_MAX_M || (p.MT - 1) * 16 >= a.M || p.MT * 16 < a.M ||
             (long long)(a.d / 128) * p.nch != p.grid)
             return hipErrorInvalidValue;
         if (norm == NORM_LN) return launch_cols<NORM_LN>(a, p, st);

@@ -40,27 +40,34 @@ __device__ __forceinline__ int rv_src(const RowView& v, int m, bool& ok) {
     ok = r >= 0 && r < v.n_src;
     return ok ? r : 0;
 }
-// For calls of at most 64 tokens, per wave: lane m holds token m's source
-// row (0 from M on), and a mask of the valid tokens.
+// For calls of at most 128 tokens, per wave: lane l holds the source rows
+// of tokens l and 64 + l (0 from M on), and masks of the valid tokens.
 struct WaveRows {
-    int src;
-    uint64_t ok;
+    int src, src_hi;
+    uint64_t ok, ok_hi;
 };
 __device__ __forceinline__ WaveRows rv_wave(const RowView& v, int M) {
     const int lane = threadIdx.x & 63;
-    bool ok = false;
-    int src = 0;
+    bool ok = false, ok_hi = false;
+    int src = 0, src_hi = 0;
     if (lane < M) src = rv_src(v, lane, ok);
+    if (64 + lane < M) src_hi = rv_src(v, 64 + lane, ok_hi);
     WaveRows w;
     w.src = src;
+    w.src_hi = src_hi;
     w.ok = __ballot(ok);
+    w.ok_hi = __ballot(ok_hi);
     return w;
 }
-// token m's source row (m < 64, any lane); m itself without an index list
+// token m's source row (m < 128, any lane); m itself without an index list
 __device__ __forceinline__ int rv_lane_src(const RowView& v, const WaveRows& w, int m) {
-    return v.idx == nullptr ? m : __shfl(w.src, m, 64);
+    if (v.idx == nullptr) return m;
+    const int lo = __shfl(w.src, m & 63, 64), hi = __shfl(w.src_hi, m & 63, 64);
+    return m < 64 ? lo : hi;
 }
-__device__ __forceinline__ bool rv_ok(const WaveRows& w, int m) { return ((w.ok >> m) & 1ull) != 0; }
+__device__ __forceinline__ bool rv_ok(const WaveRows& w, int m) {
+    return (((m < 64 ? w.ok : w.ok_hi) >> (m & 63)) & 1ull) != 0;
+}
 
 // ---------------------------------------------------------------- row stats
 // Post-norm feedback rows (out = norm(x) * gamma + beta, one row per wave).
@@ -104,6 +111,7 @@ struct DecodePlan {
 };
 
 constexpr int DECODE_MAX_M = 64;
+constexpr int GEMVN_MAX_M = 128;  // the folded column-split kernel takes up to 8 token tiles
 DecodePlan plan_decode(int M, int d, int norm);
 hipError_t launch_decode(const DecodeArgs& a, int norm, const DecodePlan& p, hipStream_t st);
 
@@ -147,7 +155,7 @@ struct GemvPlan {
     int cols = 0;   // 1: the column-split kernel (a 16-column block per wave, nch K chunks)
     int nch = 0;
     size_t counters_bytes = 0, part_bytes = 0;
-    static constexpr size_t rstats_bytes = 3 * 64 * 4 * sizeof(uint64_t);
+    static constexpr size_t rstats_bytes = 3 * GEMVN_MAX_M * 4 * sizeof(uint64_t);
 };
 
 GemvPlan plan_gemv(int M, int d, int norm);

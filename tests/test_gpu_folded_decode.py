@@ -123,6 +123,28 @@ def test_folded_decode_stats_fallback_same_bits_every_chunking(d, M, kind):
     assert_parity(bf16_to_f64(forced), oracle_out(inp, kind, eps), f"fallback d={d} M={M} kind={kind}")
 
 
+@pytest.mark.parametrize("d,M,kind", [(4096, 65, LN), (4096, 128, LN), (5120, 128, RMS), (5120, 96, LN),
+                                      (3584, 113, NONE), (8192, 100, RMS), (3072, 80, LN), (4608, 127, LN)])
+def test_folded_decode_up_to_eight_token_tiles(d, M, kind):
+    """65 to 128 tokens (5 to 8 token tiles) take the column-split decode
+    kernel where its plan exists: parity with the oracle at widths with 4, 6,
+    7 and 8 K chunks, and the forced statistics fallback gives the same bits."""
+    eps = {LN: 1e-5, RMS: 1e-6, NONE: 0.0}[kind]
+    note(f"folded decode 5-8 tiles d={d} M={M} kind={kind}")
+    w = synth.gen.custom_workload(d, (M,), seed_tag=d * 3 + M)
+    inp = synth.make_inputs(w, M)
+    dv = DevInputs(inp)
+    out, prepared = folded_call(dv, kind, eps)
+    assert_parity(bf16_to_f64(out), oracle_out(inp, kind, eps), f"folded d={d} M={M} kind={kind}")
+    if kind != NONE:
+        e31().debug_stats_recompute(True)
+        try:
+            forced, _ = folded_call(dv, kind, eps, prepared)
+        finally:
+            e31().debug_stats_recompute(False)
+        assert torch.equal(out.view(torch.int16), forced.view(torch.int16)), "fallback differs"
+
+
 @pytest.mark.parametrize("M", [4, 64])
 def test_folded_decode_dc_offset(M):
     """A shared offset of 100 sigma on h_high through the folded path: the

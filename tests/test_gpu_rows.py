@@ -164,9 +164,13 @@ def run_case(cfg, n_src, M, kind, eps, folded, layout, seed, bad=(), oracle_rows
 ALL = lambda M: np.arange(M)  # noqa: E731
 
 
-@pytest.mark.parametrize("M,layout", [(1, "interleaved"), (7, "padded"), (64, "interleaved"), (64, "padded")])
+@pytest.mark.parametrize("M,layout", [(1, "interleaved"), (7, "padded"), (64, "interleaved"), (64, "padded"),
+                                      (100, "interleaved"), (128, "padded")])
 def test_folded_decode_rows(M, layout):
-    run_case(2, 100, M, LN, 1e-5, True, layout, seed=M, oracle_rows=ALL)
+    """Up to 64 tokens the decode kernels; 100 and 128 take the column-split
+    kernel's 7 and 8 token tiles (source rows of tokens 64 .. from the second
+    per-lane register)."""
+    run_case(2, 160, M, LN, 1e-5, True, layout, seed=M, oracle_rows=ALL)
 
 
 @pytest.mark.parametrize("M,layout", [(1, "padded"), (16, "interleaved"), (61, "padded")])
@@ -187,7 +191,7 @@ def test_prefill_and_norm_kinds_rows(cfg, n_src, M, kind, eps, folded, layout):
              oracle_rows=lambda m: sample_rows(m, k=40, seed=3))
 
 
-@pytest.mark.parametrize("M,folded", [(1, True), (1, False), (40, True), (40, False), (300, True)])
+@pytest.mark.parametrize("M,folded", [(1, True), (1, False), (40, True), (40, False), (97, True), (300, True)])
 def test_indices_outside_the_buffer_give_zero_rows(M, folded):
     bad = (0,) if M == 1 else (0, M // 2, M - 1, 5)
     run_case(2, 120, M, LN, 1e-5, folded, "padded", seed=900 + M, bad=bad, oracle_rows=ALL if M < 64 else None)
