@@ -1,4 +1,5 @@
-// Decode path of the fused per-state norm + FC on the folded weight (M <= 64).
+// Decode path of the fused per-state norm + FC on the folded weight (M <= 64,
+// and up to 128 tokens in the column-split kernel).
 //
 // With the norm parameters folded into the FC (EAGLE 3.1 explainer,
 // llm-wiki.hwlabs.dev/study/dist/ai-frontier/76.html, section

@@ -212,8 +212,9 @@ int eagle31_fuse_folded_rows(const void* h_low, const void* h_mid, const void* h
  * process ends.  The call performs no allocation of its own; the caller still
  * provides every input and output.  Arguments, result and errors are those of
  * eagle31_fuse_folded, plus EAGLE31_ERR_TOO_LARGE (nothing enqueued) when the
- * problem's scratch exceeds the array: every decode call (M <= 64) up to
- * d = 8192 fits, and prefill calls whose tile count needs no split-K
+ * problem's scratch exceeds the array: every call of at most 64 tokens up to
+ * d = 8192 fits (calls of 65 to 128 tokens, whose partials grow with the
+ * token count, may not), and prefill calls whose tile count needs no split-K
  * (e.g. d = 8192, M = 4096; d = 7168, M = 32768).
  * The first call on a device also enqueues the zeroing of the array's
  * counters on `stream`.  All calls on one device share its array and each
@@ -339,7 +340,8 @@ int eagle31_release(void);
 
 /*
  * eagle31_debug_stats_recompute - test hook for the folded decode path
- * (eagle31_fuse_folded with 2 <= M <= 64; a one-token call computes the
+ * (eagle31_fuse_folded with 2 <= M <= 64, and up to 128 tokens at the widths
+ * where the column-split decode kernel takes the call; a one-token call computes the
  * statistics in every workgroup and hands nothing over, so the hook does not
  * change it).  That kernel computes each token's statistics once and hands
  * them between workgroups through the workspace;
