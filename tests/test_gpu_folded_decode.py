@@ -145,6 +145,39 @@ def test_folded_decode_up_to_eight_token_tiles(d, M, kind):
         assert torch.equal(out.view(torch.int16), forced.view(torch.int16)), "fallback differs"
 
 
+def test_folded_decode_stats_fallback_cost_is_bounded():
+    """If the workgroups that publish the statistics do not run (another
+    stream holding the CUs), a reader waits at most ~200 us and then computes
+    the rows itself.  The fallback, forced from the host, is timed here at the
+    decode batch: its cost plus the wait bound is what such a call can lose."""
+    note("stats fallback timing d=4096 M=64")
+    inp = synth.make_inputs(2, 64)
+    dv = DevInputs(inp)
+    prepared = e31().fold_prepare(LN, dv.gamma, dv.beta, dv.W, dv.bias)
+    out = torch.empty((64, dv.d), dtype=torch.bfloat16, device="cuda")
+
+    def per_call_us(n=20):
+        for _ in range(3):
+            e31().fuse_folded(dv.h[0], dv.h[1], dv.h[2], LN, 1e-5, *prepared, out=out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            e31().fuse_folded(dv.h[0], dv.h[1], dv.h[2], LN, 1e-5, *prepared, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e3
+
+    normal = per_call_us()
+    e31().debug_stats_recompute(True)
+    try:
+        forced = per_call_us()
+    finally:
+        e31().debug_stats_recompute(False)
+    print(f"[timing] folded decode d=4096 M=64: {normal:.1f} us per call, {forced:.1f} us with the statistics "
+          f"fallback in every reader", flush=True)
+    assert forced < 2000.0, f"the fallback path took {forced:.0f} us per call"
+
+
 @pytest.mark.parametrize("M", [4, 64])
 def test_folded_decode_dc_offset(M):
     """A shared offset of 100 sigma on h_high through the folded path: the
