@@ -968,15 +968,16 @@ __global__ __launch_bounds__(64 * NW) void gemvn_kernel(GemvArgs a) {
     constexpr int TB = MT < 4 ? MT : 4;
 #pragma unroll
     for (int tb = 0; tb < MT; tb += TB) {
+        // (loads unconditional, chunks past nch re-reading the last one and
+        // dropped below: a load under a branch would get a wait of its own)
         u32x4 v[GN_MAXCH][TB];
 #pragma unroll
-        for (int c = 0; c < GN_MAXCH; ++c)
-            if (c < nch) {
-                const __amdgpu_buffer_rsrc_t rs = part_rsrc(part_base(c), (int)(wtile * 16));
+        for (int c = 0; c < GN_MAXCH; ++c) {
+            const __amdgpu_buffer_rsrc_t rs = part_rsrc(part_base(min(c, nch - 1)), (int)(wtile * 16));
 #pragma unroll
-                for (int k = 0; k < TB; ++k)
-                    if (tb + k < MT) v[c][k] = load_coherent16(rs, ((tb + k) * 64 + lane) * 16);
-            }
+            for (int k = 0; k < TB; ++k)
+                if (tb + k < MT) v[c][k] = load_coherent16(rs, ((tb + k) * 64 + lane) * 16);
+        }
         f32x4 tot[TB];
 #pragma unroll
         for (int k = 0; k < TB; ++k) tot[k] = f32x4{cn, cn, cn, cn};
