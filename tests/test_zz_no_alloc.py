@@ -52,6 +52,7 @@ def pair(dv, prepared, kind, eps, M):
     (2, 4096, (64, 16), LN, 1e-5),      # decode: split-K kernel, then a smaller one
     (2, 4096, (4, 1), LN, 1e-5),        # split-K then the one-token kernel
     (3, 5120, (64, 17), RMS, 1e-6),
+    (3, 5120, (128, 96), RMS, 1e-6),    # 65 to 128 tokens: the column-split kernel, 8 then 6 token tiles
     (None, 4096, (4096, 3072), LN, 1e-5),  # prefill without split-K (statistics in the array)
 ])
 def test_noalloc_matches_fuse_folded(cfg, d, Ms, kind, eps):
@@ -78,6 +79,23 @@ def test_noalloc_matches_fuse_folded(cfg, d, Ms, kind, eps):
         bias = None if inp.bias is None else oracle.decode_bf16(inp.bias)
         Y = oracle.fuse(H, kind, eps, g, b, oracle.decode_bf16(inp.W), bias)
         assert_parity(G[rows], Y, f"no-alloc d={d} M={M}")
+
+
+def test_noalloc_refuses_decode_partials_over_the_array():
+    """128 tokens at d=4096 (8 chunks x 8 token tiles of partials: 16 MiB plus
+    counters and records) do not fit the 16 MiB array: refused before any
+    launch, while 96 tokens (6 tiles) fit and match eagle31_fuse_folded."""
+    note("no-alloc decode too large / fits")
+    w = synth.gen.custom_workload(4096, (128,), seed_tag=4111)
+    inp = synth.make_inputs(w, 128)
+    dv = DevInputs(inp)
+    prepared = e31().fold_prepare(LN, dv.gamma, dv.beta, dv.W, dv.bias)
+    out = torch.empty((128, 4096), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(e31().Eagle31Error) as ei:
+        e31().fuse_folded_noalloc(dv.h[0], dv.h[1], dv.h[2], LN, 1e-5, *prepared, out=out)
+    assert ei.value.status == e31()._capi.ERR_TOO_LARGE
+    ref, got = pair(dv, prepared, LN, 1e-5, 96)
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
 
 
 def test_noalloc_allocates_nothing():
