@@ -549,7 +549,7 @@ def main():
     achieved = dec["bytes"] / (kern_us * 1e-6) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=measured_traffic(args.M),
-                    kernel="gemvn_kernel (eagle31_fuse_folded, column split, 2<=M<=128)",
+                    kernel="gemvn_kernel (eagle31_fuse_folded, column split, up to 128 tokens)",
                     bytes_per_launch=dec["bytes"], launch_us_mean=round(kern_us, 3),
                     launch_us_mean_single_events=round(dec["event_us_mean"], 3))
 

@@ -588,29 +588,31 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_split_kernel(GemvArgs a) {
 }
 
 // =====================================================================
-// One token: one 16-column block x the whole K per workgroup
+// One or two tokens: one 16-column block x the whole K per workgroup
 // =====================================================================
 //
-// With one token the hidden states are tiny (24 KiB at d = 4096), so every
-// workgroup copies them into LDS once, computes their statistics itself (the
-// same shifted sums as the split kernel's, from LDS), and walks the whole K
-// for one 16-column block of W': no split-K partials, no counters, nothing
-// handed between workgroups (d = 4096 gives 256 workgroups, one per CU).
-// Wave w of 16 takes the k-steps w, w + 16, ... of each state in turn, one
-// accumulator per state, with an R-step W' ring; the A fragment of a step is
-// one LDS read (token rows padded by 64 bytes, so that with several tokens the
-// distinct rows would fall in different banks).  The waves' per-state tiles
-// are summed in LDS in wave order, and wave 0 applies
-// sum_s rstd_s (P_s - mu_s u_s) + c.
-constexpr int WH_MAXM = 1;  // measured: from two tokens on the split kernel is as fast
+// With one or two tokens the hidden states are small (24 KiB per token at
+// d = 4096), so every workgroup copies them into LDS once, computes their
+// statistics itself (the same shifted sums as the split kernel's, from LDS),
+// and walks the whole K for one 16-column block of W': no split-K partials,
+// no counters, nothing handed between workgroups (d = 4096 gives 256
+// workgroups, one per CU).  Wave w of 8 takes the k-steps w, w + 8, ... of
+// each state in turn, one accumulator per state, with an R-step W' ring; the
+// A fragment of a step is one LDS read (token rows padded by 64 bytes, so
+// that the distinct rows fall in different banks).  The waves' per-state
+// tiles are summed in LDS in wave order, and wave 0 applies
+// sum_s rstd_s (P_s - mu_s u_s) + c.  Measured: with four tokens the 96 KiB
+// staged per workgroup before the loop costs more than the column-split
+// kernel's hand-off.
+constexpr int WH_MAXM = 2;
 constexpr int WH_A_BYTES = WH_MAXM * (6 * 4096 + 64);  // token rows in LDS, at most
-constexpr int WH_WAVES = 16;
+constexpr int WH_WAVES = 8;
 
-template <int NORM, int R>
+template <int NORM, int R, int MM>
 __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
-    __shared__ __attribute__((aligned(16))) char la[WH_A_BYTES];
+    __shared__ __attribute__((aligned(16))) char la[MM * (6 * 4096 + 64)];
     __shared__ f32x4 red[WH_WAVES][3][64];
-    __shared__ float sst[3 * WH_MAXM][3];
+    __shared__ float sst[3 * MM][3];
     const int M = a.M, d = a.d;
     const int T3 = d >> 5, JS = T3 / WH_WAVES;  // k-steps per state and wave
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, cb = lane & 15;
@@ -619,31 +621,43 @@ __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
     if (grp >= (d >> 4)) return;
     const int rstride = 6 * d + 64;
 
-    // W' tiles of column block grp: this wave's local step j is k-step wave + 8 j
+    // The tokens' rows into LDS, states concatenated (row m: k = 0 .. 3d-1).
+    // Their loads are issued before the W' ring's, every one of them (a
+    // thread's surplus chunks wrap round to chunks already taken, spread
+    // over the rows), so the LDS writes wait for these loads alone and the
+    // ring stays in flight across the staging barrier.
+    constexpr int ACH = MM * (3 * 4096 / 8) / (64 * WH_WAVES);  // 16-byte chunks per thread
+    const int cpr = (3 * d) >> 3, cps = d >> 3;  // 16-byte chunks per row / per state
+    const int nchunk = M * cpr;
+    const WaveRows wr = rv_wave(a.rv, M);
+    u32x4 av[ACH];
+    int aoff[ACH];
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+        int v = tid + i * 64 * WH_WAVES;
+        v = v < nchunk ? v : v % nchunk;
+        const int m = v / cpr, c = v - m * cpr;
+        const int st = (c >= cps) + (c >= 2 * cps);
+        const size_t srow = (size_t)rv_lane_src(a.rv, wr, m);
+        const uint16_t* base = st == 0 ? a.h[0] + srow * (size_t)a.rv.ld[0]
+                                       : (st == 1 ? a.h[1] + srow * (size_t)a.rv.ld[1] : a.h[2] + srow * (size_t)a.rv.ld[2]);
+        av[i] = *reinterpret_cast<const u32x4*>(base + 8 * (c - st * cps));
+        aoff[i] = m * rstride + c * 16;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // W' tiles of column block grp: this wave's local step j is k-step
+    // wave + WH_WAVES j
     const u32x4* __restrict__ wp = reinterpret_cast<const u32x4*>(a.wp) + ((size_t)grp * 3 * T3 + wave) * 64 + lane;
     constexpr int WSTEP = WH_WAVES * 64;  // uint4 between a wave's steps
     u32x4 rw[R];
 #pragma unroll
     for (int p = 0; p < R; ++p) rw[p] = __builtin_nontemporal_load(&wp[(size_t)p * WSTEP]);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // token rows into LDS, states concatenated (row m: k = 0 .. 3d-1): the
-    // token's source row of each state
-    static_assert(WH_MAXM == 1, "the staging below reads one token's rows");
-    const WaveRows wr = rv_wave(a.rv, M);
-    {
-        const size_t srow = (size_t)rv_lane_src(a.rv, wr, 0);
-        const uint64_t r0 = reinterpret_cast<uint64_t>(a.h[0] + srow * (size_t)a.rv.ld[0]);
-        const uint64_t rd1 = reinterpret_cast<uint64_t>(a.h[1] + srow * (size_t)a.rv.ld[1]) - r0;
-        const uint64_t rd2 = reinterpret_cast<uint64_t>(a.h[2] + srow * (size_t)a.rv.ld[2]) - r0;
-        const int cpr = (3 * d) >> 3, cps = d >> 3;  // 16-byte chunks per row / per state
-        for (int v = tid; v < M * cpr; v += 64 * WH_WAVES) {
-            const int m = v / cpr, c = v - m * cpr;
-            const int st = (c >= cps) + (c >= 2 * cps);
-            const uint64_t base = r0 + (uint64_t)(st == 1) * rd1 + (uint64_t)(st == 2) * rd2;
-            const uint16_t* src = reinterpret_cast<const uint16_t*>(base) + 8 * (c - st * cps);
-            *reinterpret_cast<uint4*>(la + m * rstride + c * 16) = *reinterpret_cast<const uint4*>(src);
-        }
-    }
+#pragma unroll
+    for (int i = 0; i < ACH; ++i)
+        if (tid + i * 64 * WH_WAVES < nchunk) *reinterpret_cast<u32x4*>(la + aoff[i]) = av[i];
     __syncthreads();
 
     // statistics of the 3M (state, token) rows: wave w takes rows w, w + 8
@@ -1007,9 +1021,8 @@ GemvPlan plan_gemv(int M, int d, int norm) {
     p.MT = (M + 15) / 16;
     const int T3 = d / 32;
     // a handful of tokens: the whole-K kernel when its token rows fit in LDS
-    // and its one-block-per-workgroup grid fills whole rounds of the CUs
-    if (M <= WH_MAXM && d % (32 * WH_WAVES) == 0 && M * (6 * d + 64) <= WH_A_BYTES &&
-        (d / 16 <= 256 || (d / 16) % 256 == 0)) {
+    // (one workgroup per 16-column block, at most one round of the CUs)
+    if (M <= WH_MAXM && d <= 4096 && d % (32 * WH_WAVES) == 0 && M * (6 * d + 64) <= WH_A_BYTES) {
         const int JS = T3 / WH_WAVES;
         int ring = 8;
         while (ring > 1 && (JS % ring || JS < ring)) ring >>= 1;
@@ -1130,16 +1143,25 @@ static hipError_t launch_gn(const GemvArgs& a, const GemvPlan& p, hipStream_t st
     }
 }
 
+// token-row slots staged per workgroup: 1 or 2 (d <= 4096)
+template <int NORM, int R>
+static hipError_t launch_whole_mm(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
+    if (a.M == 1)
+        gemv_whole_kernel<NORM, R, 1><<<p.grid, 64 * WH_WAVES, 0, st>>>(a);
+    else
+        gemv_whole_kernel<NORM, R, 2><<<p.grid, 64 * WH_WAVES, 0, st>>>(a);
+    return hipGetLastError();
+}
+
 template <int NORM>
 static hipError_t launch_whole(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
     switch (p.ring) {
-        case 8: gemv_whole_kernel<NORM, 8><<<p.grid, 64 * WH_WAVES, 0, st>>>(a); break;
-        case 4: gemv_whole_kernel<NORM, 4><<<p.grid, 64 * WH_WAVES, 0, st>>>(a); break;
-        case 2: gemv_whole_kernel<NORM, 2><<<p.grid, 64 * WH_WAVES, 0, st>>>(a); break;
-        case 1: gemv_whole_kernel<NORM, 1><<<p.grid, 64 * WH_WAVES, 0, st>>>(a); break;
+        case 8: return launch_whole_mm<NORM, 8>(a, p, st);
+        case 4: return launch_whole_mm<NORM, 4>(a, p, st);
+        case 2: return launch_whole_mm<NORM, 2>(a, p, st);
+        case 1: return launch_whole_mm<NORM, 1>(a, p, st);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 template <int NORM>
@@ -1171,8 +1193,8 @@ hipError_t launch_gemv(const GemvArgs& a, int norm, const GemvPlan& p, hipStream
         return launch_cols<NORM_NONE>(a, p, st);
     }
     if (p.whole) {
-        if (a.M < 1 || a.M > WH_MAXM || a.M * (6 * a.d + 64) > WH_A_BYTES || a.d % (32 * WH_WAVES) ||
-            p.grid != a.d / 16)
+        if (a.M < 1 || a.M > WH_MAXM || a.d > 4096 || a.M * (6 * a.d + 64) > WH_A_BYTES || a.d % (32 * WH_WAVES) ||
+            p.grid != a.d / 16 || (a.d / 32 / WH_WAVES) % p.ring || a.d / 32 / WH_WAVES < p.ring)
             return hipErrorInvalidValue;
         if (norm == NORM_LN) return launch_whole<NORM_LN>(a, p, st);
         if (norm == NORM_RMS) return launch_whole<NORM_RMS>(a, p, st);

@@ -1,4 +1,4 @@
-"""The folded decode path (eagle31_fuse_folded, 2 <= M <= 64) against the
+"""The folded decode path (eagle31_fuse_folded, 1 <= M <= 128) against the
 fp64 oracle through the C ABI, at every token-tile count and at widths that
 change the split-K kernel's plan (columns per workgroup, waves, chunks per
 state, ring depth), for all three norms; the decode-shaped workloads at every
@@ -66,6 +66,23 @@ def test_folded_decode_parity(d, M):
     dv = DevInputs(inp)
     out, _ = folded_call(dv, kind, eps)
     assert_parity(bf16_to_f64(out), oracle_out(inp, kind, eps), f"folded d={d} M={M} kind={kind}")
+
+
+@pytest.mark.parametrize("d", [512, 1280, 2304, 4096])
+@pytest.mark.parametrize("M", [1, 2, 3, 4])
+def test_whole_k_kernel_few_tokens(d, M):
+    """1 to 4 tokens at widths up to 4096: with one or two tokens each
+    workgroup stages the tokens' rows into LDS (chunk counts that do not fill
+    a whole number of loads per thread wrap round) and walks the whole K for
+    one 16-column block; three and four tokens take the split kernels."""
+    kind = (LN, RMS, NONE)[(d // 256 + M) % 3]
+    eps = {LN: 1e-5, RMS: 1e-6, NONE: 0.0}[kind]
+    note(f"whole-K decode d={d} M={M} kind={kind}")
+    w = synth.gen.custom_workload(d, (M,), seed_tag=d * 7 + M)
+    inp = synth.make_inputs(w, M)
+    dv = DevInputs(inp)
+    out, _ = folded_call(dv, kind, eps)
+    assert_parity(bf16_to_f64(out), oracle_out(inp, kind, eps), f"whole-K d={d} M={M} kind={kind}")
 
 
 @pytest.mark.parametrize("kind", [LN, RMS, NONE])

@@ -164,12 +164,13 @@ def run_case(cfg, n_src, M, kind, eps, folded, layout, seed, bad=(), oracle_rows
 ALL = lambda M: np.arange(M)  # noqa: E731
 
 
-@pytest.mark.parametrize("M,layout", [(1, "interleaved"), (7, "padded"), (64, "interleaved"), (64, "padded"),
-                                      (100, "interleaved"), (128, "padded")])
+@pytest.mark.parametrize("M,layout", [(1, "interleaved"), (3, "padded"), (4, "interleaved"), (7, "padded"),
+                                      (64, "interleaved"), (64, "padded"), (100, "interleaved"), (128, "padded")])
 def test_folded_decode_rows(M, layout):
-    """Up to 64 tokens the decode kernels; 100 and 128 take the column-split
-    kernel's 7 and 8 token tiles (source rows of tokens 64 .. from the second
-    per-lane register)."""
+    """Up to 64 tokens the decode kernels (one or two tokens staged whole
+    into each workgroup's LDS); 100 and 128 take the column-split kernel's 7 and 8
+    token tiles (source rows of tokens 64 .. from the second per-lane
+    register)."""
     run_case(2, 160, M, LN, 1e-5, True, layout, seed=M, oracle_rows=ALL)
 
 
