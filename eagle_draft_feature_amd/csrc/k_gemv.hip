@@ -767,6 +767,280 @@ __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
 }
 
 // =====================================================================
+// Up to 4 tokens, packed token blocks: one 16-column block x the whole K
+// =====================================================================
+//
+// The MFMA's 16 A rows hold at most 4 tokens here, so the rows past the
+// tokens are spare.  A wave's token loads use them: lane (g, cb) of a
+// "packed block" holds token row cb % MP (MP = 16 / SB, a power of two at
+// or above M) of the wave's k-step t0 + cb / MP, 16 bytes of k-group g.  One
+// 16-byte load per lane thus brings SB of the wave's k-steps for every
+// token (SB = 16 at one token, 4 at three or four), and the A fragment of
+// k-step t0 + j is the block moved j * MP lanes down each 16-lane row (a DPP
+// row shift; rows past the tokens then hold junk whose MFMA rows are never
+// read).  Each lane feeds its block's values once to the row statistics
+// (shifted sums; shift K = mean of the row's first 32 values), so the
+// statistics cost one pass over the tokens' values per workgroup, spread
+// through the loop, and no token bytes are staged before it.  Otherwise as
+// the whole-K kernel: one 16-column block of W' per workgroup (d = 4096: 256
+// workgroups), wave w of 8 takes the k-steps w, w + 8, ... of each state in
+// turn with an 8-step W' ring, the waves' tiles and statistics are summed in
+// LDS in wave order, and wave 0 applies sum_s rstd_s (P_s - mu_s u_s) + c.
+// Measured: from five tokens on, every workgroup's pass over all the tokens'
+// values costs more than the column-split kernel's hand-off.
+constexpr int PK_MAXM = 4;
+constexpr int PK_WAVES = 8;
+constexpr int PK_R = 8;
+
+// v moved down by n lanes within each 16-lane row (lane i takes lane i + n;
+// lanes past the row's end get 0)
+__device__ __forceinline__ uint32_t row_shl_u32(uint32_t v, int n) {
+    switch (n) {
+        case 0: return v;
+        case 1: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x101, 0xf, 0xf, true);
+        case 2: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x102, 0xf, 0xf, true);
+        case 3: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x103, 0xf, 0xf, true);
+        case 4: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x104, 0xf, 0xf, true);
+        case 5: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x105, 0xf, 0xf, true);
+        case 6: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x106, 0xf, 0xf, true);
+        case 7: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x107, 0xf, 0xf, true);
+        case 8: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x108, 0xf, 0xf, true);
+        case 9: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x109, 0xf, 0xf, true);
+        case 10: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x10a, 0xf, 0xf, true);
+        case 11: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x10b, 0xf, 0xf, true);
+        case 12: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x10c, 0xf, 0xf, true);
+        case 13: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x10d, 0xf, 0xf, true);
+        case 14: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x10e, 0xf, 0xf, true);
+        default: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x10f, 0xf, 0xf, true);
+    }
+}
+
+// sum over the lanes of each 16-lane row whose index is equal modulo MP
+// (DPP row rotations by 8, 4, .. MP); every such lane ends with the sum
+template <int MP>
+__device__ __forceinline__ float row_mod_sum(float v) {
+    if (MP <= 8) v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+    if (MP <= 4) v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false));
+    if (MP <= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false));
+    if (MP <= 1) v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false));
+    return v;
+}
+
+template <int NORM, int SB>
+__global__ __launch_bounds__(64 * PK_WAVES) void gemv_pack_kernel(GemvArgs a) {
+    constexpr int R = PK_R, MP = 16 / SB, U = SB > R ? SB : R, NBB = U / SB;  // U: steps per body
+    __shared__ f32x4 red[PK_WAVES][3][64];
+    __shared__ float sred[PK_WAVES][3][MP][2];
+    __shared__ float smr[3][MP][2];
+    const int M = a.M, d = a.d;
+    const int T3 = d >> 5, JS = T3 / PK_WAVES;  // k-steps per state; per state and wave
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, cb = lane & 15;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = blockIdx.x;
+    if (grp >= (d >> 4)) return;
+    const int n = 16 * grp + cb;  // this lane's output column
+    const WaveRows wr = rv_wave(a.rv, M);
+
+    // packed-block lane (g, cb): step offset jl = cb / MP, token row rl = cb % MP
+    const int jl = cb / MP, rl = cb % MP;
+    const bool rvalid = rl < M;
+    const size_t brow = (size_t)rv_lane_src(a.rv, wr, min(rl, M - 1));
+    // state s's block of the wave's local steps [t, t + SB): bs + 512 t
+    const char* const b0 = reinterpret_cast<const char*>(a.h[0] + brow * (size_t)a.rv.ld[0]) + 16 * g + 64 * (wave + 8 * jl);
+    const char* const b1 = reinterpret_cast<const char*>(a.h[1] + brow * (size_t)a.rv.ld[1]) + 16 * g + 64 * (wave + 8 * jl);
+    const char* const b2 = reinterpret_cast<const char*>(a.h[2] + brow * (size_t)a.rv.ld[2]) + 16 * g + 64 * (wave + 8 * jl);
+    constexpr int BSTEP = 64 * PK_WAVES;  // bytes between a wave's steps
+
+    // shift rows (LayerNorm): lane (g, cb) holds token cb's values 8 g .. of
+    // each state's first k-step; c and u of this lane's column
+    u32x4 kf0 = {0u, 0u, 0u, 0u}, kf1 = kf0, kf2 = kf0;
+    if (NORM == NORM_LN) {
+        const size_t frow = (size_t)rv_lane_src(a.rv, wr, min(cb, M - 1));
+        kf0 = *reinterpret_cast<const u32x4*>(a.h[0] + frow * (size_t)a.rv.ld[0] + 8 * g);
+        kf1 = *reinterpret_cast<const u32x4*>(a.h[1] + frow * (size_t)a.rv.ld[1] + 8 * g);
+        kf2 = *reinterpret_cast<const u32x4*>(a.h[2] + frow * (size_t)a.rv.ld[2] + 8 * g);
+    }
+    const float cn = a.c[n];
+    float un[3] = {0.f, 0.f, 0.f};
+    if (NORM == NORM_LN) {
+#pragma unroll
+        for (int q = 0; q < 3; ++q) un[q] = a.u[(size_t)q * d + n];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // rings: the first body's packed blocks, then the W' ring
+    u32x4 ab[NBB];
+#pragma unroll
+    for (int bb = 0; bb < NBB; ++bb) ab[bb] = *reinterpret_cast<const u32x4*>(b0 + bb * SB * BSTEP);
+    const u32x4* __restrict__ wp = reinterpret_cast<const u32x4*>(a.wp) + ((size_t)grp * 3 * T3 + wave) * 64 + lane;
+    constexpr int WSTEP = PK_WAVES * 64;  // uint4 between a wave's steps
+    u32x4 rw[R];
+#pragma unroll
+    for (int p = 0; p < R; ++p) {
+        rw[p] = __builtin_nontemporal_load(&wp[(size_t)p * WSTEP]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // per-lane shifts of the packed lanes' token rows
+    float kb[3] = {0.f, 0.f, 0.f};
+    if (NORM == NORM_LN) {
+        const u32x4 kf[3] = {kf0, kf1, kf2};
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            float v = ((bf_lo(kf[q][0]) + bf_hi(kf[q][0])) + (bf_lo(kf[q][1]) + bf_hi(kf[q][1]))) +
+                      ((bf_lo(kf[q][2]) + bf_hi(kf[q][2])) + (bf_lo(kf[q][3]) + bf_hi(kf[q][3])));
+            v += __shfl_xor(v, 16, 64);
+            v += __shfl_xor(v, 32, 64);
+            const float K = v * (1.0f / 32.0f);  // token cb's shift
+            if (wave == 0 && g == 0 && cb < M && cb < MP) smr[q][cb][0] = K;
+            kb[q] = __shfl(K, rl, 64);
+        }
+    }
+
+    f32x4 acc[3];
+    float s1[3] = {0.f, 0.f, 0.f}, s2[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 3; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // one body of U steps of state s starting at local step i: per packed
+    // block its statistics, its SB fragments and the prefetch of the block U
+    // steps on (from anext when that lies in the next state), then SB steps.
+    // refill: 0 none, 1 W' and blocks, 2 W' only for steps whose target is
+    // still inside the call (the last body of the last state)
+    auto body = [&](f32x4& ac, float& x1s, float& x2s, float k, int j0, int i, const char* anext, int nexti,
+                    int refill) __attribute__((always_inline)) {
+#pragma unroll
+        for (int bb = 0; bb < NBB; ++bb) {
+            if (NORM != NORM_NONE) {
+                float t1 = 0.f, t2 = 0.f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float x0 = bf_lo(ab[bb][e]), x1 = bf_hi(ab[bb][e]);
+                    if (NORM == NORM_LN) {
+                        x0 -= k;
+                        x1 -= k;
+                        t1 += x0 + x1;
+                    }
+                    t2 = fmaf(x0, x0, fmaf(x1, x1, t2));
+                }
+                x1s += rvalid ? t1 : 0.f;
+                x2s += rvalid ? t2 : 0.f;
+            }
+            // fragments of steps 1 .. SB-1; step 0 reads the block itself,
+            // after which its registers take the block U steps on
+            u32x4 fr[SB];
+#pragma unroll
+            for (int j = 1; j < SB; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) fr[j][e] = row_shl_u32(ab[bb][e], j * MP);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < SB; ++j) {
+                const int p = bb * SB + j;
+                ac = mfma16x16x32(j == 0 ? ab[bb] : fr[j], rw[p % R], ac);
+                if (refill == 1 || (refill == 2 && p + R < U))
+                    rw[p % R] = __builtin_nontemporal_load(&wp[(size_t)(j0 + i + p + R) * WSTEP]);
+                if (j == 0 && refill == 1) ab[bb] = *reinterpret_cast<const u32x4*>(anext + (nexti + bb * SB) * BSTEP);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+    // one state: JS / U bodies; the last one's prefetches target the next
+    // state (or, in the last state, only what is left of it)
+    auto run_state = [&](f32x4& ac, float& x1s, float& x2s, float k, int j0, const char* acur, const char* anext,
+                         bool last) __attribute__((always_inline)) {
+        int i = 0;
+        for (; i < JS - U; i += U) body(ac, x1s, x2s, k, j0, i, acur, i + U, 1);
+        if (last)
+            body(ac, x1s, x2s, k, j0, i, acur, 0, 2);
+        else
+            body(ac, x1s, x2s, k, j0, i, anext, 0, 1);
+    };
+    run_state(acc[0], s1[0], s2[0], kb[0], 0, b0, b1, false);
+    run_state(acc[1], s1[1], s2[1], kb[1], JS, b1, b2, false);
+    run_state(acc[2], s1[2], s2[2], kb[2], 2 * JS, b2, b2, true);
+
+    // the tiles, and the statistics summed over each token row's lanes
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        red[wave][q][lane] = acc[q];
+        if (NORM != NORM_NONE) {
+            s1[q] = row_mod_sum<MP>(s1[q]);
+            s2[q] = row_mod_sum<MP>(s2[q]);
+        }
+    }
+    if (NORM != NORM_NONE) {
+        float t1[3], t2[3];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            t1[q] = __shfl_xor(s1[q], 16, 64);
+            t2[q] = __shfl_xor(s2[q], 16, 64);
+        }
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            s1[q] += t1[q];
+            s2[q] += t2[q];
+        }
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            t1[q] = __shfl_xor(s1[q], 32, 64);
+            t2[q] = __shfl_xor(s2[q], 32, 64);
+        }
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            if (lane < MP) {
+                sred[wave][q][lane][0] = s1[q] + t1[q];
+                sred[wave][q][lane][1] = s2[q] + t2[q];
+            }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    // (mu, rstd) of (state q, token r) by lane MP q + r, into LDS for the
+    // lanes that apply them (the same wave: its LDS accesses complete in order)
+    if (NORM != NORM_NONE && lane < 3 * MP && (lane % MP) < M) {
+        const int q = lane / MP, r = lane % MP;
+        float S1 = 0.f, S2 = 0.f;
+#pragma unroll
+        for (int w = 0; w < PK_WAVES; ++w) {
+            S1 += sred[w][q][r][0];
+            S2 += sred[w][q][r][1];
+        }
+        const float st[3] = {NORM == NORM_LN ? smr[q][r][0] : 0.f, S1, S2};
+        float mu, rs;
+        row_norm<NORM>(st, d, a.eps, mu, rs);
+        smr[q][r][0] = mu;
+        smr[q][r][1] = rs;
+    }
+    __builtin_amdgcn_wave_barrier();
+    f32x4 P[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        P[q] = red[0][q][lane];
+#pragma unroll
+        for (int w = 1; w < PK_WAVES; ++w) P[q] += red[w][q][lane];
+    }
+    // lane (g, cb): rows 4 g + e, column n
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int m = 4 * g + e;
+        if (m >= M) continue;
+        float y = cn;
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            float mu = 0.f, r = 1.f;
+            if (NORM != NORM_NONE) {
+                mu = smr[q][m][0];
+                r = smr[q][m][1];
+            }
+            float pv = P[q][e];
+            if (NORM == NORM_LN) pv -= mu * un[q];
+            y += (NORM == NORM_NONE) ? pv : r * pv;
+        }
+        a.out[(size_t)m * (size_t)a.rv.ld_out + n] = rv_ok(wr, m) ? (uint16_t)(pack_bf2(y, 0.f) & 0xffffu) : (uint16_t)0;
+    }
+}
+
+// =====================================================================
 // Column split: one 16-column block per wave over a K chunk
 // =====================================================================
 //
@@ -1020,6 +1294,23 @@ GemvPlan plan_gemv(int M, int d, int norm) {
     GemvPlan p;
     p.MT = (M + 15) / 16;
     const int T3 = d / 32;
+    // up to 4 tokens where each wave's k-steps per state are a multiple of 8
+    // (d = 2048, 4096): the packed-block whole-K kernel
+    if (M <= PK_MAXM && d % (32 * PK_WAVES) == 0 && d <= 4096 && (d / 32 / PK_WAVES) % PK_R == 0) {
+        const int JS = T3 / PK_WAVES;
+        int mp = 1;
+        while (mp < M) mp <<= 1;
+        p.pack = 1;
+        p.sb = std::min(16 / mp, JS);
+        p.ring = PK_R;
+        p.waves = PK_WAVES;
+        p.kps = 1;
+        p.nb = 1;
+        p.grid = d / 16;
+        p.counters_bytes = 256;
+        p.part_bytes = 256;
+        return p;
+    }
     // a handful of tokens: the whole-K kernel when its token rows fit in LDS
     // (one workgroup per 16-column block, at most one round of the CUs)
     if (M <= WH_MAXM && d <= 4096 && d % (32 * WH_WAVES) == 0 && M * (6 * d + 64) <= WH_A_BYTES) {
@@ -1181,7 +1472,30 @@ static hipError_t launch_cols(const GemvArgs& a, const GemvPlan& p, hipStream_t 
     return hipGetLastError();
 }
 
+template <int NORM>
+static hipError_t launch_pack(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
+    switch (p.sb) {
+        case 16: gemv_pack_kernel<NORM, 16><<<p.grid, 64 * PK_WAVES, 0, st>>>(a); break;
+        case 8: gemv_pack_kernel<NORM, 8><<<p.grid, 64 * PK_WAVES, 0, st>>>(a); break;
+        case 4: gemv_pack_kernel<NORM, 4><<<p.grid, 64 * PK_WAVES, 0, st>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gemv(const GemvArgs& a, int norm, const GemvPlan& p, hipStream_t st) {
+    if (p.pack) {
+        // the kernel's fixed shape: k-steps per wave and state a multiple of
+        // its 8-step ring and of its body (max(sb, 8) steps), every token a row
+        // slot (16 / sb of them), one workgroup per 16-column block
+        const int JS = a.d / 32 / PK_WAVES, body = std::max(p.sb, PK_R);
+        if (a.M < 1 || a.M > PK_MAXM || a.d > 4096 || a.d % (32 * PK_WAVES) || p.sb < 4 || p.sb > 16 ||
+            a.M > 16 / p.sb || JS % body || p.sb > JS || p.grid != a.d / 16)
+            return hipErrorInvalidValue;
+        if (norm == NORM_LN) return launch_pack<NORM_LN>(a, p, st);
+        if (norm == NORM_RMS) return launch_pack<NORM_RMS>(a, p, st);
+        return launch_pack<NORM_NONE>(a, p, st);
+    }
     if (p.cols) {
         const int T = 3 * a.d / 32, body = std::max(GN_RW, 16);
         if (p.waves != 8 || a.nch != p.nch || p.nch < 1 || p.nch > GN_MAXCH || a.d % 128 || T % (p.nch * body) ||

@@ -153,7 +153,8 @@ struct GemvPlan {
     int kps = 0, ring = 0, waves = 0, nb = 4, MT = 1, grid = 0;  // nb: 16-column blocks per workgroup
     int whole = 0;  // 1: few tokens, the whole-K kernel (one 16-column block per workgroup, no split)
     int cols = 0;   // 1: the column-split kernel (a 16-column block per wave, nch K chunks)
-    int nch = 0;
+    int pack = 0;   // 1: few tokens, the packed-block whole-K kernel; sb: its k-steps per packed block
+    int nch = 0, sb = 0;
     size_t counters_bytes = 0, part_bytes = 0;
     static constexpr size_t rstats_bytes = 3 * GEMVN_MAX_M * 4 * sizeof(uint64_t);
 };

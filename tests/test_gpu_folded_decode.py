@@ -68,13 +68,15 @@ def test_folded_decode_parity(d, M):
     assert_parity(bf16_to_f64(out), oracle_out(inp, kind, eps), f"folded d={d} M={M} kind={kind}")
 
 
-@pytest.mark.parametrize("d", [512, 1280, 2304, 4096])
+@pytest.mark.parametrize("d", [512, 1280, 2048, 2304, 4096])
 @pytest.mark.parametrize("M", [1, 2, 3, 4])
 def test_whole_k_kernel_few_tokens(d, M):
-    """1 to 4 tokens at widths up to 4096: with one or two tokens each
-    workgroup stages the tokens' rows into LDS (chunk counts that do not fill
-    a whole number of loads per thread wrap round) and walks the whole K for
-    one 16-column block; three and four tokens take the split kernels."""
+    """1 to 4 tokens at widths up to 4096, each workgroup walking the whole K
+    for one 16-column block: at d = 2048 and 4096 with packed token blocks
+    (16, 8 or 4 k-steps per load; at d = 2048 one token takes two row slots),
+    elsewhere with one or two tokens staged into LDS (chunk counts that do not
+    fill a whole number of loads per thread wrap round) and three or four on
+    the split kernels."""
     kind = (LN, RMS, NONE)[(d // 256 + M) % 3]
     eps = {LN: 1e-5, RMS: 1e-6, NONE: 0.0}[kind]
     note(f"whole-K decode d={d} M={M} kind={kind}")
@@ -96,25 +98,27 @@ def test_folded_decode_every_norm_at_the_headline_shape(kind):
 
 
 def test_folded_decode_bitwise_over_many_calls():
-    """Fifty calls back to back on one stream, at two token counts in turn:
-    every output is bit-identical to the first of its size."""
-    note("folded decode 50 repeats")
+    """Fifty-one calls back to back on one stream, at three token counts in
+    turn (column split, and packed token blocks at three tokens): every output
+    is bit-identical to the first of its size."""
+    note("folded decode 51 repeats")
     inp = synth.make_inputs(2, 64)
     dv = DevInputs(inp)
     prepared = e31().fold_prepare(LN, dv.gamma, dv.beta, dv.W, dv.bias)
     refs = {}
-    for M in (64, 9):
+    for M in (64, 9, 3):
         h = [x[:M] for x in dv.h]
         refs[M] = e31().fuse_folded(h[0], h[1], h[2], LN, 1e-5, *prepared)
     outs = []
-    for i in range(50):
-        M = 64 if i % 2 == 0 else 9
+    for i in range(51):
+        M = (64, 9, 3)[i % 3]
         h = [x[:M] for x in dv.h]
         outs.append((M, e31().fuse_folded(h[0], h[1], h[2], LN, 1e-5, *prepared)))
     torch.cuda.synchronize()
     for M, o in outs:
         assert torch.equal(o.view(torch.int16), refs[M].view(torch.int16)), f"repeat differs at M={M}"
     assert_parity(bf16_to_f64(refs[9]), oracle_out(inp.rows(9), LN, 1e-5), "folded M=9")
+    assert_parity(bf16_to_f64(refs[3]), oracle_out(inp.rows(3), LN, 1e-5), "folded M=3")
 
 
 @pytest.mark.parametrize("d,M,kind", [(3584, 64, LN), (3584, 17, NONE), (5120, 33, RMS), (8192, 2, LN),
