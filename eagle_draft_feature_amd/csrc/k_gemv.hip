@@ -767,15 +767,15 @@ __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
 }
 
 // =====================================================================
-// Up to 4 tokens, packed token blocks: one 16-column block x the whole K
+// Up to 6 tokens, packed token blocks: one 16-column block x the whole K
 // =====================================================================
 //
-// The MFMA's 16 A rows hold at most 4 tokens here, so the rows past the
+// The MFMA's 16 A rows hold at most 6 tokens here, so the rows past the
 // tokens are spare.  A wave's token loads use them: lane (g, cb) of a
 // "packed block" holds token row cb % MP (MP = 16 / SB, a power of two at
 // or above M) of the wave's k-step t0 + cb / MP, 16 bytes of k-group g.  One
 // 16-byte load per lane thus brings SB of the wave's k-steps for every
-// token (SB = 16 at one token, 4 at three or four), and the A fragment of
+// token (SB = 16 at one token, 2 at five or six), and the A fragment of
 // k-step t0 + j is the block moved j * MP lanes down each 16-lane row (a DPP
 // row shift; rows past the tokens then hold junk whose MFMA rows are never
 // read).  Each lane feeds its block's values once to the row statistics
@@ -786,9 +786,9 @@ __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
 // workgroups), wave w of 8 takes the k-steps w, w + 8, ... of each state in
 // turn with an 8-step W' ring, the waves' tiles and statistics are summed in
 // LDS in wave order, and wave 0 applies sum_s rstd_s (P_s - mu_s u_s) + c.
-// Measured: from five tokens on, every workgroup's pass over all the tokens'
-// values costs more than the column-split kernel's hand-off.
-constexpr int PK_MAXM = 4;
+// Measured: from seven tokens on, every workgroup's pass over all the
+// tokens' values costs as much as the column-split kernel's hand-off.
+constexpr int PK_MAXM = 6;
 constexpr int PK_WAVES = 8;
 constexpr int PK_R = 8;
 
@@ -1294,7 +1294,7 @@ GemvPlan plan_gemv(int M, int d, int norm) {
     GemvPlan p;
     p.MT = (M + 15) / 16;
     const int T3 = d / 32;
-    // up to 4 tokens where each wave's k-steps per state are a multiple of 8
+    // up to 6 tokens where each wave's k-steps per state are a multiple of 8
     // (d = 2048, 4096): the packed-block whole-K kernel
     if (M <= PK_MAXM && d % (32 * PK_WAVES) == 0 && d <= 4096 && (d / 32 / PK_WAVES) % PK_R == 0) {
         const int JS = T3 / PK_WAVES;
@@ -1478,6 +1478,7 @@ static hipError_t launch_pack(const GemvArgs& a, const GemvPlan& p, hipStream_t 
         case 16: gemv_pack_kernel<NORM, 16><<<p.grid, 64 * PK_WAVES, 0, st>>>(a); break;
         case 8: gemv_pack_kernel<NORM, 8><<<p.grid, 64 * PK_WAVES, 0, st>>>(a); break;
         case 4: gemv_pack_kernel<NORM, 4><<<p.grid, 64 * PK_WAVES, 0, st>>>(a); break;
+        case 2: gemv_pack_kernel<NORM, 2><<<p.grid, 64 * PK_WAVES, 0, st>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1489,7 +1490,7 @@ hipError_t launch_gemv(const GemvArgs& a, int norm, const GemvPlan& p, hipStream
         // its 8-step ring and of its body (max(sb, 8) steps), every token a row
         // slot (16 / sb of them), one workgroup per 16-column block
         const int JS = a.d / 32 / PK_WAVES, body = std::max(p.sb, PK_R);
-        if (a.M < 1 || a.M > PK_MAXM || a.d > 4096 || a.d % (32 * PK_WAVES) || p.sb < 4 || p.sb > 16 ||
+        if (a.M < 1 || a.M > PK_MAXM || a.d > 4096 || a.d % (32 * PK_WAVES) || p.sb < 2 || p.sb > 16 ||
             a.M > 16 / p.sb || JS % body || p.sb > JS || p.grid != a.d / 16)
             return hipErrorInvalidValue;
         if (norm == NORM_LN) return launch_pack<NORM_LN>(a, p, st);

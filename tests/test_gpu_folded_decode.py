@@ -69,14 +69,14 @@ def test_folded_decode_parity(d, M):
 
 
 @pytest.mark.parametrize("d", [512, 1280, 2048, 2304, 4096])
-@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 6])
 def test_whole_k_kernel_few_tokens(d, M):
-    """1 to 4 tokens at widths up to 4096, each workgroup walking the whole K
+    """1 to 6 tokens at widths up to 4096, each workgroup walking the whole K
     for one 16-column block: at d = 2048 and 4096 with packed token blocks
-    (16, 8 or 4 k-steps per load; at d = 2048 one token takes two row slots),
-    elsewhere with one or two tokens staged into LDS (chunk counts that do not
-    fill a whole number of loads per thread wrap round) and three or four on
-    the split kernels."""
+    (16, 8, 4 or 2 k-steps per load; at d = 2048 one token takes two row
+    slots), elsewhere with one or two tokens staged into LDS (chunk counts
+    that do not fill a whole number of loads per thread wrap round) and more
+    on the split kernels."""
     kind = (LN, RMS, NONE)[(d // 256 + M) % 3]
     eps = {LN: 1e-5, RMS: 1e-6, NONE: 0.0}[kind]
     note(f"whole-K decode d={d} M={M} kind={kind}")
