@@ -381,6 +381,7 @@ int run_fuse(const Rows& R, int64_t M, int64_t d, int norm, float eps, const voi
     a.d = (int)d;
     a.norm = norm;
     a.splits = p.splits;
+    a.chunks = p.chunks;
     a.part = at<float>(ws, L.part);
     e = launch_prefill(a, p, st);
     if (e != hipSuccess) return hip_fail(e);

@@ -27,9 +27,11 @@
 // M-tiles, and consecutive workgroup ids are spread so that each XCD
 // (workgroup id mod 8) takes a contiguous run of that order: the tiles an
 // XCD runs at once share A and B tiles in its L2.
-// Few tiles (small M) split K by chunks that never cross a state; the chunks'
-// partials go to the workspace and a reduction kernel launched next on the
-// stream sums them in a fixed order and applies the statistics.
+// Few tiles (small M) split K into chunks, each inside one state (or, with 43
+// to 64 tiles, four equal chunks across the states, which store one partial
+// per state part); the partials go to the workspace and a reduction kernel
+// launched next on the stream sums each state's parts in a fixed order and
+// applies the statistics.
 #include <algorithm>
 
 #include "common.hpp"
@@ -150,7 +152,7 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
     // the newest 2 stages of loads (8 per wave each) are complete
     constexpr int WAIT_STAGE = wait_vm(16);
 
-    const TileCoord tc = map_tile(blockIdx.x, TM, TN, SPLIT ? a.splits : 1);
+    const TileCoord tc = map_tile(blockIdx.x, TM, TN, SPLIT ? a.chunks : 1);
     if (!tc.valid) return;
     const int M = a.M, d = a.d;
     const int m0 = tc.mt * PBM, n0 = tc.nt * PBN;
@@ -159,7 +161,12 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
     const int wm = wave >> 1, wn = wave & 1;
     const int KTS = d / PBK;  // sub-tiles per state
     int kt0 = 0, kt1 = 3 * KTS;
-    if (SPLIT) {
+    if (SPLIT && a.chunks != a.splits) {
+        // four equal chunks across the states (sub-tiles 3 KTS c / 4 ..): each
+        // state gets two parts, the first from the state's start
+        kt0 = (tc.chunk * 3 * KTS) / 4;
+        kt1 = ((tc.chunk + 1) * 3 * KTS) / 4;
+    } else if (SPLIT) {
         const int kps = a.splits / 3;
         const int s = tc.chunk / kps, j = tc.chunk - s * kps;
         kt0 = s * KTS + (j * KTS) / kps;
@@ -331,11 +338,27 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
         asm volatile("s_barrier" ::: "memory");
     };
     // When every state's sub-tile count is a multiple of 4 (and always for a
-    // split-K chunk, which lies in one state), the pipeline runs on across the
-    // state boundaries: the loads near the end of a state already fetch the
-    // next one and each state starts on stage 0 again.  Otherwise it restarts
-    // at every state.
+    // split-K chunk: one inside a state, or one of four across the states with
+    // every part a multiple of 4), the pipeline runs on across the state
+    // boundaries: the loads near the end of a state already fetch the next one
+    // and each state starts on stage 0 again.  Otherwise it restarts at every
+    // state.
     const bool cont = SPLIT || (KTS & 3) == 0;
+    // a split chunk's partial of state s's part starting at sub-tile ua, in
+    // fragment order (rows from M on are skipped); slot: the chunk, or with
+    // chunks across the states 2 s + (0 for the part that starts the state)
+    auto store_part = [&](int s, int ua) __attribute__((always_inline)) {
+        const int tile = tc.mt * TN + tc.nt;
+        const int slot = a.chunks != a.splits ? 2 * s + (ua == s * KTS ? 0 : 1) : tc.chunk;
+        const size_t frag_per_wg = (size_t)PTH * 64;  // f32x4 per (tile, slot)
+        f32x4* mine = reinterpret_cast<f32x4*>(a.part) + ((size_t)tile * a.splits + slot) * frag_per_wg;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (m0 + wm * 128 + 16 * i >= M) continue;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mine[((size_t)(i * 8 + j) * 4 + wave) * 64 + lane] = acc[i][j];
+        }
+    };
     for (int s = kt0 / KTS; s < 3 && s * KTS < kt1; ++s) {
         const int ua = max(kt0, s * KTS), ub = min(kt1, (s + 1) * KTS);
         const int lim = cont ? kt1 : ub;  // loads stay below lim
@@ -367,23 +390,24 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
             if (u + 3 < ub) sub_step(u + 3, lim, st3, st0, 1);
         }
         if (!SPLIT && NORM != NORM_NONE && s < 2) rescale(s);
+        if (SPLIT && ub < kt1) {
+            // a chunk across the states: this state's part is done
+            store_part(s, ua);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
     // the last sub-steps' loads (re-reads near the end) land before the
     // workgroup can end and its LDS be handed to another
     __builtin_amdgcn_s_waitcnt(0);
 
     if (SPLIT) {
-        // this chunk's partial in fragment order; the reduction kernel that
-        // runs next on the stream sums the chunks (rows from M on are skipped)
-        const int tile = tc.mt * TN + tc.nt;
-        const size_t frag_per_wg = (size_t)PTH * 64;  // f32x4 per (tile, chunk)
-        f32x4* mine = reinterpret_cast<f32x4*>(a.part) + ((size_t)tile * a.splits + tc.chunk) * frag_per_wg;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if (m0 + wm * 128 + 16 * i >= M) continue;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) mine[((size_t)(i * 8 + j) * 4 + wave) * 64 + lane] = acc[i][j];
-        }
+        // the chunk's (last) partial; the reduction kernel that runs next on
+        // the stream sums each state's parts in order
+        const int sl = (kt1 - 1) / KTS;
+        store_part(sl, max(kt0, sl * KTS));
         return;
     }
 
@@ -495,6 +519,14 @@ PrefillPlan plan_prefill(int M, int d) {
         const int KTS = d / PBK;
         const int kps = std::max(1, std::min(std::min(8, KTS), 256 / (3 * tiles)));
         p.splits = 3 * kps;
+        p.chunks = p.splits;
+        // 43 to 64 tiles: one chunk per state would leave a quarter or more of
+        // the CUs idle, two a second round; four equal chunks across the states
+        // (two parts per state, each a multiple of 4 sub-tiles) fill up to 256
+        if (kps == 1 && 4 * tiles <= 256 && KTS % 16 == 0) {
+            p.splits = 6;
+            p.chunks = 4;
+        }
     }
     if (p.splits > 1) p.part_bytes = (size_t)tiles * p.splits * PTH * 64 * sizeof(f32x4);
     return p;
@@ -502,7 +534,7 @@ PrefillPlan plan_prefill(int M, int d) {
 
 template <bool SPLIT, int NORM>
 static hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& p, hipStream_t st) {
-    const int items = p.tiles_m * p.tiles_n * (SPLIT ? p.splits : 1);
+    const int items = p.tiles_m * p.tiles_n * (SPLIT ? p.chunks : 1);
     const int grid = ((items + 7) / 8) * 8;
     if (a.rv.ld[0] == a.rv.ld[1] && a.rv.ld[1] == a.rv.ld[2])
         prefill_kernel<SPLIT, NORM, true><<<grid, PTH, 0, st>>>(a, p.tiles_m, p.tiles_n);

@@ -183,12 +183,13 @@ struct PrefillArgs {
     RowView rv;
     int M, d;
     int norm;
-    int splits;           // 1 or a multiple of 3
+    int splits;           // partial slots per tile: 1 (no split) or 3 x (parts per state)
+    int chunks;           // K chunks (workgroups) per tile: splits, or 4 chunks that cross the states
     float* part;          // split-K partials (summed by a second kernel)
 };
 
 struct PrefillPlan {
-    int splits = 1;
+    int splits = 1, chunks = 1;
     int tiles_m = 0, tiles_n = 0;
     size_t part_bytes = 0;
 };

@@ -136,6 +136,29 @@ def test_prefill_state_restart_ragged(folded):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("d,M,kind", [(7168, 512, LN), (4096, 700, RMS), (8192, 300, LN)])
+def test_prefill_four_chunks_across_states(d, M, kind):
+    """43 to 64 output tiles: K split into four equal chunks that cross the
+    state boundaries, each storing one partial per state part (56, 48 and 64
+    tiles; M = 700 and 300 leave ragged last M-tiles).  Both entry points,
+    every row against the oracle, and the same bits on a second call."""
+    eps = {LN: 1e-5, RMS: 1e-6}[kind]
+    note(f"prefill four chunks d={d} M={M} kind={kind}")
+    w = synth.gen.custom_workload(d, (M,), seed_tag=d + M)
+    inp = synth.make_inputs(w, M)
+    dv = DevInputs(inp)
+    Y = oracle_rows(inp, kind, eps)
+    wf, u, c = e31().fold_prepare(kind, dv.gamma, dv.beta, dv.W, dv.bias)
+    F1 = e31().fuse_folded(dv.h[0], dv.h[1], dv.h[2], kind, eps, wf, u, c)
+    F2 = e31().fuse_folded(dv.h[0], dv.h[1], dv.h[2], kind, eps, wf, u, c)
+    torch.cuda.synchronize()
+    assert torch.equal(F1.view(torch.int16), F2.view(torch.int16)), "second call differs"
+    assert_parity(bf16_to_f64(F1), Y, f"four chunks folded d={d} M={M}")
+    assert_parity(run_fuse(dv, kind, eps), Y, f"four chunks stored W d={d} M={M}")
+    del dv, wf, u, c, F1, F2
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------ the fold path
 @pytest.mark.parametrize("cfg,kind,eps", [(1, LN, 1e-5), (3, RMS, 1e-6), (1, NONE, 0.0)])
 def test_fold_prepare_exact_weight_and_vectors(cfg, kind, eps):

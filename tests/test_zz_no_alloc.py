@@ -49,8 +49,9 @@ def pair(dv, prepared, kind, eps, M):
 
 
 @pytest.mark.parametrize("cfg,d,Ms,kind,eps", [
-    (2, 4096, (64, 16), LN, 1e-5),      # decode: split-K kernel, then a smaller one
-    (2, 4096, (4, 1), LN, 1e-5),        # split-K then the one-token kernel
+    (2, 4096, (64, 16), LN, 1e-5),      # decode: the column-split kernel, 4 then 1 token tiles
+    (2, 4096, (8, 6), LN, 1e-5),        # the column split, then packed token blocks (no scratch)
+    (2, 4096, (4, 1), LN, 1e-5),        # packed token blocks, 4 then 1 token
     (3, 5120, (64, 17), RMS, 1e-6),
     (3, 5120, (128, 96), RMS, 1e-6),    # 65 to 128 tokens: the column-split kernel, 8 then 6 token tiles
     (None, 4096, (4096, 3072), LN, 1e-5),  # prefill without split-K (statistics in the array)
