@@ -1295,8 +1295,11 @@ GemvPlan plan_gemv(int M, int d, int norm) {
     p.MT = (M + 15) / 16;
     const int T3 = d / 32;
     // up to 6 tokens where each wave's k-steps per state are a multiple of 8
-    // (d = 2048, 4096): the packed-block whole-K kernel
-    if (M <= PK_MAXM && d % (32 * PK_WAVES) == 0 && d <= 4096 && (d / 32 / PK_WAVES) % PK_R == 0) {
+    // (d = 2048, 4096): the packed-block whole-K kernel; one token also where
+    // its grid is whole rounds of the CUs (d = 8192: 64.5 us against 67.9 on
+    // the split kernel; from two tokens on the column split is as fast there)
+    if (M <= PK_MAXM && d % (32 * PK_WAVES) == 0 && (d <= 4096 || (M == 1 && (d / 16) % 256 == 0)) &&
+        (d / 32 / PK_WAVES) % PK_R == 0) {
         const int JS = T3 / PK_WAVES;
         int mp = 1;
         while (mp < M) mp <<= 1;
@@ -1490,7 +1493,7 @@ hipError_t launch_gemv(const GemvArgs& a, int norm, const GemvPlan& p, hipStream
         // its 8-step ring and of its body (max(sb, 8) steps), every token a row
         // slot (16 / sb of them), one workgroup per 16-column block
         const int JS = a.d / 32 / PK_WAVES, body = std::max(p.sb, PK_R);
-        if (a.M < 1 || a.M > PK_MAXM || a.d > 4096 || a.d % (32 * PK_WAVES) || p.sb < 2 || p.sb > 16 ||
+        if (a.M < 1 || a.M > PK_MAXM || (a.d > 4096 && (a.M != 1 || (a.d / 16) % 256)) || a.d % (32 * PK_WAVES) || p.sb < 2 || p.sb > 16 ||
             a.M > 16 / p.sb || JS % body || p.sb > JS || p.grid != a.d / 16)
             return hipErrorInvalidValue;
         if (norm == NORM_LN) return launch_pack<NORM_LN>(a, p, st);

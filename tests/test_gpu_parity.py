@@ -354,9 +354,10 @@ def test_two_streams_use_their_own_workspaces():
 @pytest.mark.parametrize("d", [512, 1024, 2048, 3072, 4096, 5120, 8192])
 @pytest.mark.parametrize("kind", [LN, RMS, NONE])
 def test_one_token_kernel_widths(d, kind):
-    """A single token goes through the whole-K kernel (one 16-column block per
-    workgroup, statistics from each workgroup's LDS copy of the token): at
-    widths that change its ring depth and grid, for every norm."""
+    """A single token at widths that change the one-token plan, for every
+    norm: packed token blocks at d = 2048, 4096 and 8192 (two rounds of
+    workgroups), the LDS-staged whole-K kernel at 512, 1024 and 3072, the
+    split-K kernel at 5120."""
     note(f"one token d={d} kind={kind}")
     w = synth.gen.custom_workload(d, (1,), seed_tag=d + 7 * kind)
     inp = synth.make_inputs(w, 1)
