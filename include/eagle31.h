@@ -341,9 +341,10 @@ int eagle31_release(void);
 /*
  * eagle31_debug_stats_recompute - test hook for the folded decode path
  * (eagle31_fuse_folded with 2 <= M <= 64, and up to 128 tokens at the widths
- * where the column-split decode kernel takes the call; calls of one token, and of
- * two at widths up to 4096, compute the statistics in every workgroup and hand
- * nothing over, so the hook does not change them).  That kernel computes each
+ * where the column-split decode kernel takes the call; calls of up to six tokens
+ * at d = 2048 and 4096, of one token at d = 8192 and of one or two at the other
+ * widths up to 4096 compute the statistics in every workgroup and hand nothing
+ * over, so the hook does not change them).  That kernel computes each
  * token's statistics once and hands
  * them between workgroups through the workspace;
  * a reader waits a bounded time for them and, if they are not there, computes
