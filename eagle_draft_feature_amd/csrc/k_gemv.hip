@@ -274,14 +274,26 @@ __device__ __forceinline__ void row_norm(const float (&st)[3], int d, float eps,
 // 3M) as (mu, rstd) into out[row] once its record carries this call's id
 // (the same bounded wait and the same fallback as stats_gather, so the same
 // bits).  One round trip when the records are there.
-template <int NORM>
-__device__ void stats_gather_rows(const GemvArgs& a, int lane, int first, float (*out)[2], const WaveRows& wr) {
+// PRE: the caller loaded row it's three words earlier (p0, p1, p2); they
+// are enough when all carry this call's id, and otherwise the wait below runs.
+template <int NORM, bool PRE>
+__device__ void stats_gather_rows(const GemvArgs& a, int lane, int first, float (*out)[2], const WaveRows& wr,
+                                  uint64_t p0, uint64_t p1, uint64_t p2) {
     const int need = 3 * a.M;
     const int it = min(first + lane, need - 1);
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     bool ready = false;
     uint64_t w[3];
-    for (; !a.stats_recompute;) {
+    if constexpr (PRE) {
+        w[0] = p0;
+        w[1] = p1;
+        w[2] = p2;
+        bool mine = !a.stats_recompute;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) mine &= (uint32_t)(w[k] >> 32) == a.call_id;
+        ready = __all(mine);
+    }
+    if (!ready) for (; !a.stats_recompute;) {
 #pragma unroll
         for (int k = 0; k < 3; ++k) w[k] = rec_load(a.rstats + 4 * it + k);
         bool mine = true;
@@ -1163,7 +1175,20 @@ __global__ __launch_bounds__(64 * NW) void gemvn_kernel(GemvArgs a) {
     f32x4 acc[MT], accs[MT];
 #pragma unroll
     for (int tt = 0; tt < MT; ++tt) acc[tt] = accs[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // with one or two token tiles the statistics records (published long
+    // before) are loaded at the start of the last body, beside its W' loads,
+    // so the gather after the loop finds them in registers (measured: no gain
+    // with four tiles, where the gather loads them itself)
+    uint64_t pw0 = 0, pw1 = 0, pw2 = 0;
     for (int b0 = 0; b0 < nsteps; b0 += BODY) {
+        if constexpr (MT <= 2) {
+            if (b0 == nsteps - BODY) {
+                const uint64_t* rp = a.rstats + 4 * min(64 * wave + lane, 3 * M - 1);
+                pw0 = rec_load(rp);
+                pw1 = rec_load(rp + 1);
+                pw2 = rec_load(rp + 2);
+            }
+        }
 #pragma unroll
         for (int gi = 0; gi < BODY / NW; ++gi) {
             const int G = b0 / NW + gi;  // group index
@@ -1202,7 +1227,8 @@ __global__ __launch_bounds__(64 * NW) void gemvn_kernel(GemvArgs a) {
 
     // statistics (published long before): wave w gathers rows 64 w ..
     // 64 w + 63 and turns each row's sums into (mu, rstd) for the workgroup
-    if (NORM != NORM_NONE && 64 * wave < 3 * M) stats_gather_rows<NORM>(a, lane, 64 * wave, sh_mr, wr);
+    if (NORM != NORM_NONE && 64 * wave < 3 * M)
+        stats_gather_rows<NORM, (MT <= 2)>(a, lane, 64 * wave, sh_mr, wr, pw0, pw1, pw2);
     __syncthreads();
     // this wave's contribution of the chunk, sum over its state parts of
     // rstd_s (P - mu_s u_s) (P for no norm), fragment order, stored at the
