@@ -796,13 +796,23 @@ __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
 // through the loop, and no token bytes are staged before it.  Otherwise as
 // the whole-K kernel: one 16-column block of W' per workgroup (d = 4096: 256
 // workgroups), wave w of 8 takes the k-steps w, w + 8, ... of each state in
-// turn with an 8-step W' ring, the waves' tiles and statistics are summed in
-// LDS in wave order, and wave 0 applies sum_s rstd_s (P_s - mu_s u_s) + c.
+// turn with an 8- or 16-step W' ring.  Each wave publishes a state's tile
+// rows that can hold tokens and its per-token statistics to LDS as soon as
+// the state is done (lane sums by DPP and gfx950 permlane swaps, no LDS round
+// trip); after one barrier wave 0 issues all its LDS reads at once, sums the
+// waves in a fixed tree, broadcasts (mu, rstd) by readlane and applies
+// sum_s rstd_s (P_s - mu_s u_s) + c.
 // Measured: from seven tokens on, every workgroup's pass over all the
 // tokens' values costs as much as the column-split kernel's hand-off.
 constexpr int PK_MAXM = 6;
 constexpr int PK_WAVES = 8;
-constexpr int PK_R = 8;
+constexpr int PK_R = 8;  // W' ring depth, and the least k-steps per wave and state
+// One token at d <= 4096 (blocks of 16 k-steps, one workgroup per CU): a
+// 16-step ring, which kept the loop fed better (17.7 against 18.1 us at
+// d = 4096).  Elsewhere it was as fast or slower: six tokens 20.5 against
+// 20.1 us; one token at d = 8192 (two workgroups per CU in turn) 68.0
+// against 64.7.
+inline int pk_ring(int sb, int d) { return sb == 16 && d <= 4096 ? 16 : PK_R; }
 
 // v moved down by n lanes within each 16-lane row (lane i takes lane i + n;
 // lanes past the row's end get 0)
@@ -838,12 +848,25 @@ __device__ __forceinline__ float row_mod_sum(float v) {
     return v;
 }
 
-template <int NORM, int SB>
+// v plus the value of the lane 16 (32) apart, in every lane: one gfx950
+// permlane swap of v with itself hands each lane its partner's value, with no
+// LDS round trip (the whole wave must be active)
+__device__ __forceinline__ float xor16_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int NORM, int SB, int R>
 __global__ __launch_bounds__(64 * PK_WAVES) void gemv_pack_kernel(GemvArgs a) {
-    constexpr int R = PK_R, MP = 16 / SB, U = SB > R ? SB : R, NBB = U / SB;  // U: steps per body
-    __shared__ f32x4 red[PK_WAVES][3][64];
-    __shared__ float sred[PK_WAVES][3][MP][2];
-    __shared__ float smr[3][MP][2];
+    constexpr int MP = 16 / SB, U = SB > R ? SB : R, NBB = U / SB;  // U: steps per body
+    constexpr int NG = (MP + 3) / 4;  // 16-lane row groups of a tile that hold token rows
+    __shared__ f32x4 red[PK_WAVES][3][16 * NG];
+    __shared__ __align__(16) float sred[3][MP][PK_WAVES][2];
+    __shared__ float smk[3][MP];
     const int M = a.M, d = a.d;
     const int T3 = d >> 5, JS = T3 / PK_WAVES;  // k-steps per state; per state and wave
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, cb = lane & 15;
@@ -863,14 +886,13 @@ __global__ __launch_bounds__(64 * PK_WAVES) void gemv_pack_kernel(GemvArgs a) {
     const char* const b2 = reinterpret_cast<const char*>(a.h[2] + brow * (size_t)a.rv.ld[2]) + 16 * g + 64 * (wave + 8 * jl);
     constexpr int BSTEP = 64 * PK_WAVES;  // bytes between a wave's steps
 
-    // shift rows (LayerNorm): lane (g, cb) holds token cb's values 8 g .. of
-    // each state's first k-step; c and u of this lane's column
+    // shift rows (LayerNorm): lane (g, cb) holds the values 8 g .. of each
+    // state's first k-step of its own token row; c and u of this lane's column
     u32x4 kf0 = {0u, 0u, 0u, 0u}, kf1 = kf0, kf2 = kf0;
     if (NORM == NORM_LN) {
-        const size_t frow = (size_t)rv_lane_src(a.rv, wr, min(cb, M - 1));
-        kf0 = *reinterpret_cast<const u32x4*>(a.h[0] + frow * (size_t)a.rv.ld[0] + 8 * g);
-        kf1 = *reinterpret_cast<const u32x4*>(a.h[1] + frow * (size_t)a.rv.ld[1] + 8 * g);
-        kf2 = *reinterpret_cast<const u32x4*>(a.h[2] + frow * (size_t)a.rv.ld[2] + 8 * g);
+        kf0 = *reinterpret_cast<const u32x4*>(a.h[0] + brow * (size_t)a.rv.ld[0] + 8 * g);
+        kf1 = *reinterpret_cast<const u32x4*>(a.h[1] + brow * (size_t)a.rv.ld[1] + 8 * g);
+        kf2 = *reinterpret_cast<const u32x4*>(a.h[2] + brow * (size_t)a.rv.ld[2] + 8 * g);
     }
     const float cn = a.c[n];
     float un[3] = {0.f, 0.f, 0.f};
@@ -901,11 +923,10 @@ __global__ __launch_bounds__(64 * PK_WAVES) void gemv_pack_kernel(GemvArgs a) {
         for (int q = 0; q < 3; ++q) {
             float v = ((bf_lo(kf[q][0]) + bf_hi(kf[q][0])) + (bf_lo(kf[q][1]) + bf_hi(kf[q][1]))) +
                       ((bf_lo(kf[q][2]) + bf_hi(kf[q][2])) + (bf_lo(kf[q][3]) + bf_hi(kf[q][3])));
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            const float K = v * (1.0f / 32.0f);  // token cb's shift
-            if (wave == 0 && g == 0 && cb < M && cb < MP) smr[q][cb][0] = K;
-            kb[q] = __shfl(K, rl, 64);
+            v = xor32_sum(xor16_sum(v));
+            const float K = v * (1.0f / 32.0f);  // the shift of token row rl
+            if (wave == 0 && g == 0 && cb < MP) smk[q][cb] = K;
+            kb[q] = K;
         }
     }
 
@@ -968,87 +989,107 @@ __global__ __launch_bounds__(64 * PK_WAVES) void gemv_pack_kernel(GemvArgs a) {
         else
             body(ac, x1s, x2s, k, j0, i, anext, 0, 1);
     };
-    run_state(acc[0], s1[0], s2[0], kb[0], 0, b0, b1, false);
-    run_state(acc[1], s1[1], s2[1], kb[1], JS, b1, b2, false);
-    run_state(acc[2], s1[2], s2[2], kb[2], 2 * JS, b2, b2, true);
-
-    // the tiles, and the statistics summed over each token row's lanes
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-        red[wave][q][lane] = acc[q];
+    // a state's share for the cross-wave sums, once its steps are done: the
+    // tile rows that can hold tokens (row groups below NG), and each token
+    // row's statistics summed over its lanes (DPP within the 16-lane rows,
+    // then the two cross-row swaps); states 0 and 1 while the next state's
+    // loads are in flight
+    auto publish = [&](int q) __attribute__((always_inline)) {
+        if (g < NG) red[wave][q][lane] = acc[q];
         if (NORM != NORM_NONE) {
-            s1[q] = row_mod_sum<MP>(s1[q]);
-            s2[q] = row_mod_sum<MP>(s2[q]);
+            const float x1 = xor32_sum(xor16_sum(row_mod_sum<MP>(s1[q])));
+            const float x2 = xor32_sum(xor16_sum(row_mod_sum<MP>(s2[q])));
+            if (lane < MP) *reinterpret_cast<float2*>(&sred[q][lane][wave][0]) = make_float2(x1, x2);
         }
-    }
-    if (NORM != NORM_NONE) {
-        float t1[3], t2[3];
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            t1[q] = __shfl_xor(s1[q], 16, 64);
-            t2[q] = __shfl_xor(s2[q], 16, 64);
-        }
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            s1[q] += t1[q];
-            s2[q] += t2[q];
-        }
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            t1[q] = __shfl_xor(s1[q], 32, 64);
-            t2[q] = __shfl_xor(s2[q], 32, 64);
-        }
-#pragma unroll
-        for (int q = 0; q < 3; ++q)
-            if (lane < MP) {
-                sred[wave][q][lane][0] = s1[q] + t1[q];
-                sred[wave][q][lane][1] = s2[q] + t2[q];
-            }
-    }
+    };
+    run_state(acc[0], s1[0], s2[0], kb[0], 0, b0, b1, false);
+    publish(0);
+    run_state(acc[1], s1[1], s2[1], kb[1], JS, b1, b2, false);
+    publish(1);
+    run_state(acc[2], s1[2], s2[2], kb[2], 2 * JS, b2, b2, true);
+    publish(2);
     __syncthreads();
     if (wave != 0) return;
-    // (mu, rstd) of (state q, token r) by lane MP q + r, into LDS for the
-    // lanes that apply them (the same wave: its LDS accesses complete in order)
-    if (NORM != NORM_NONE && lane < 3 * MP && (lane % MP) < M) {
-        const int q = lane / MP, r = lane % MP;
+
+    // wave 0. Lane (g, cb) sums WPL waves' tiles of row group g mod NG (waves
+    // WPL (g / NG) ..), and the lanes of one row group are then summed across
+    // rows: a fixed tree over the 8 waves. Lane MP q + r turns the sums of
+    // (state q, token r) into (mu, rstd) (lanes past 3 MP take state 2's, unused).
+    // Every LDS read is issued before any is used: one round trip.
+    constexpr int WPL = PK_WAVES * NG / 4;
+    const int gg = g % NG, w0 = (g / NG) * WPL;
+    const int qs = min(lane / MP, 2), r = lane % MP;
+    // only the tile elements that can hold a token are read (rows e < MP),
+    // each into registers of its own
+    constexpr int EU = MP < 4 ? MP : 4;
+    float tv[3][WPL][EU];
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int w = 0; w < WPL; ++w)
+#pragma unroll
+            for (int e = 0; e < EU; ++e) tv[q][w][e] = reinterpret_cast<const float*>(&red[w0 + w][q][16 * gg + cb])[e];
+    f32x4 sv[PK_WAVES / 2];  // (S1, S2) of waves 2 i and 2 i + 1
+    float kq = 0.f;
+    if (NORM != NORM_NONE) {
+#pragma unroll
+        for (int i = 0; i < PK_WAVES / 2; ++i) sv[i] = reinterpret_cast<const f32x4*>(&sred[qs][r][0][0])[i];
+        if (NORM == NORM_LN) kq = smk[qs][r];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float P[3][EU];
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int e = 0; e < EU; ++e) {
+            P[q][e] = tv[q][0][e];
+#pragma unroll
+            for (int w = 1; w < WPL; ++w) P[q][e] += tv[q][w][e];
+        }
+    float mu = 0.f, rs = 1.f;
+    if (NORM != NORM_NONE) {
         float S1 = 0.f, S2 = 0.f;
 #pragma unroll
-        for (int w = 0; w < PK_WAVES; ++w) {
-            S1 += sred[w][q][r][0];
-            S2 += sred[w][q][r][1];
+        for (int i = 0; i < PK_WAVES / 2; ++i) {
+            S1 += sv[i][0];
+            S2 += sv[i][1];
+            S1 += sv[i][2];
+            S2 += sv[i][3];
         }
-        const float st[3] = {NORM == NORM_LN ? smr[q][r][0] : 0.f, S1, S2};
-        float mu, rs;
+        const float st[3] = {kq, S1, S2};
         row_norm<NORM>(st, d, a.eps, mu, rs);
-        smr[q][r][0] = mu;
-        smr[q][r][1] = rs;
     }
-    __builtin_amdgcn_wave_barrier();
-    f32x4 P[3];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-        P[q] = red[0][q][lane];
+    for (int q = 0; q < 3; ++q)
 #pragma unroll
-        for (int w = 1; w < PK_WAVES; ++w) P[q] += red[w][q][lane];
-    }
-    // lane (g, cb): rows 4 g + e, column n
+        for (int e = 0; e < EU; ++e) {
+            if (NG == 1) P[q][e] = xor16_sum(P[q][e]);
+            P[q][e] = xor32_sum(P[q][e]);
+        }
+    // lane (g, cb): rows 4 g + e, column n; (mu, rstd) of a row read from
+    // its lane (the same for the whole wave)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < EU; ++e) {
         const int m = 4 * g + e;
-        if (m >= M) continue;
         float y = cn;
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
-            float mu = 0.f, r = 1.f;
+            float muq = 0.f, rq = 1.f;
             if (NORM != NORM_NONE) {
-                mu = smr[q][m][0];
-                r = smr[q][m][1];
+                muq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mu), MP * q + e));
+                rq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rs), MP * q + e));
+                if (NG == 2) {
+                    const float mu1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mu), MP * q + 4 + e));
+                    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rs), MP * q + 4 + e));
+                    muq = g == 1 ? mu1 : muq;
+                    rq = g == 1 ? r1 : rq;
+                }
             }
             float pv = P[q][e];
-            if (NORM == NORM_LN) pv -= mu * un[q];
-            y += (NORM == NORM_NONE) ? pv : r * pv;
+            if (NORM == NORM_LN) pv -= muq * un[q];
+            y += (NORM == NORM_NONE) ? pv : rq * pv;
         }
-        a.out[(size_t)m * (size_t)a.rv.ld_out + n] = rv_ok(wr, m) ? (uint16_t)(pack_bf2(y, 0.f) & 0xffffu) : (uint16_t)0;
+        if (m < M) a.out[(size_t)m * (size_t)a.rv.ld_out + n] = rv_ok(wr, m) ? (uint16_t)(pack_bf2(y, 0.f) & 0xffffu) : (uint16_t)0;
     }
 }
 
@@ -1331,7 +1372,7 @@ GemvPlan plan_gemv(int M, int d, int norm) {
         while (mp < M) mp <<= 1;
         p.pack = 1;
         p.sb = std::min(16 / mp, JS);
-        p.ring = PK_R;
+        p.ring = pk_ring(p.sb, d);
         p.waves = PK_WAVES;
         p.kps = 1;
         p.nb = 1;
@@ -1504,10 +1545,13 @@ static hipError_t launch_cols(const GemvArgs& a, const GemvPlan& p, hipStream_t 
 template <int NORM>
 static hipError_t launch_pack(const GemvArgs& a, const GemvPlan& p, hipStream_t st) {
     switch (p.sb) {
-        case 16: gemv_pack_kernel<NORM, 16><<<p.grid, 64 * PK_WAVES, 0, st>>>(a); break;
-        case 8: gemv_pack_kernel<NORM, 8><<<p.grid, 64 * PK_WAVES, 0, st>>>(a); break;
-        case 4: gemv_pack_kernel<NORM, 4><<<p.grid, 64 * PK_WAVES, 0, st>>>(a); break;
-        case 2: gemv_pack_kernel<NORM, 2><<<p.grid, 64 * PK_WAVES, 0, st>>>(a); break;
+        case 16:
+            if (p.ring == 16) gemv_pack_kernel<NORM, 16, 16><<<p.grid, 64 * PK_WAVES, 0, st>>>(a);
+            else gemv_pack_kernel<NORM, 16, PK_R><<<p.grid, 64 * PK_WAVES, 0, st>>>(a);
+            break;
+        case 8: gemv_pack_kernel<NORM, 8, PK_R><<<p.grid, 64 * PK_WAVES, 0, st>>>(a); break;
+        case 4: gemv_pack_kernel<NORM, 4, PK_R><<<p.grid, 64 * PK_WAVES, 0, st>>>(a); break;
+        case 2: gemv_pack_kernel<NORM, 2, PK_R><<<p.grid, 64 * PK_WAVES, 0, st>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -1516,11 +1560,11 @@ static hipError_t launch_pack(const GemvArgs& a, const GemvPlan& p, hipStream_t 
 hipError_t launch_gemv(const GemvArgs& a, int norm, const GemvPlan& p, hipStream_t st) {
     if (p.pack) {
         // the kernel's fixed shape: k-steps per wave and state a multiple of
-        // its 8-step ring and of its body (max(sb, 8) steps), every token a row
+        // its ring and of its body (max(sb, ring) steps), every token a row
         // slot (16 / sb of them), one workgroup per 16-column block
-        const int JS = a.d / 32 / PK_WAVES, body = std::max(p.sb, PK_R);
+        const int JS = a.d / 32 / PK_WAVES, body = std::max(p.sb, p.ring);
         if (a.M < 1 || a.M > PK_MAXM || (a.d > 4096 && (a.M != 1 || (a.d / 16) % 256)) || a.d % (32 * PK_WAVES) || p.sb < 2 || p.sb > 16 ||
-            a.M > 16 / p.sb || JS % body || p.sb > JS || p.grid != a.d / 16)
+            a.M > 16 / p.sb || (p.ring != PK_R && !(p.ring == 16 && p.sb == 16)) || JS % body || p.sb > JS || p.grid != a.d / 16)
             return hipErrorInvalidValue;
         if (norm == NORM_LN) return launch_pack<NORM_LN>(a, p, st);
         if (norm == NORM_RMS) return launch_pack<NORM_RMS>(a, p, st);
