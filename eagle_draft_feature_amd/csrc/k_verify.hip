@@ -99,27 +99,40 @@ __device__ __forceinline__ void band_flush(Band& a, Dig& d) {
         a.b[i] = 0;
     }
 }
-__device__ __forceinline__ Dig dig_shfl_up(const Dig& a, int delta) {
-    Dig r;
-#pragma unroll
-    for (int i = 0; i < VF_ND; ++i) {
-        const uint32_t lo = __shfl_up((uint32_t)a.d[i], delta, 64), hi = __shfl_up((uint32_t)(a.d[i] >> 32), delta, 64);
-        r.d[i] = ((uint64_t)hi << 32) | lo;
-    }
-    return r;
+// One DPP move of both halves of a 64-bit value (CTRL a DPP control code;
+// lanes whose source lies outside their row, or whose row ROWS masks off,
+// read 0): cross-lane traffic in registers, no LDS round trip.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWS, 0xf, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWS, 0xf, true);
+    return ((uint64_t)hi << 32) | lo;
 }
-__device__ __forceinline__ Dig dig_shfl_xor(const Dig& a, int mask) {
-    Dig r;
-#pragma unroll
-    for (int i = 0; i < VF_ND; ++i) {
-        const uint32_t lo = __shfl_xor((uint32_t)a.d[i], mask, 64), hi = __shfl_xor((uint32_t)(a.d[i] >> 32), mask, 64);
-        r.d[i] = ((uint64_t)hi << 32) | lo;
-    }
-    return r;
+// v plus the value of the lane 16 (32) apart: a gfx950 permlane swap of each
+// half with itself hands every lane the pair (its own value, its partner's)
+__device__ __forceinline__ uint64_t xor16_sum64(uint64_t v) {
+    const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    return (((uint64_t)hi[0] << 32) | lo[0]) + (((uint64_t)hi[1] << 32) | lo[1]);
 }
+__device__ __forceinline__ uint64_t xor32_sum64(uint64_t v) {
+    const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+    return (((uint64_t)hi[0] << 32) | lo[0]) + (((uint64_t)hi[1] << 32) | lo[1]);
+}
+// the digits summed over the 64 lanes, in every lane (integer adds: any order
+// gives the same bits): row rotations by 8, 4, 2, 1, then the two cross-row
+// swaps.  The whole wave must be active.
 __device__ __forceinline__ Dig dig_wave_sum(Dig a) {
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) dig_add(a, dig_shfl_xor(a, o));
+    for (int i = 0; i < VF_ND; ++i) {
+        uint64_t v = a.d[i];
+        v += dpp64<0x128>(v);
+        v += dpp64<0x124>(v);
+        v += dpp64<0x122>(v);
+        v += dpp64<0x121>(v);
+        a.d[i] = xor32_sum64(xor16_sum64(v));
+    }
     return a;
 }
 // carry-propagated digits
@@ -372,13 +385,21 @@ __device__ void wave_range_sum(const WRow& r, int qa, int qlen, Dig& acc, uint32
     acc = dig_wave_sum(acc);
 }
 
-// inclusive scan of Dig over the 64 lanes
+// inclusive scan of Dig over the 64 lanes: within each 16-lane row by DPP
+// row shifts of 1, 2, 4, 8, then row r's total (its lane 15) added to row
+// r + 1 (rows 1 and 3), then lane 31's (rows 0-1) to rows 2 and 3.  The
+// whole wave must be active.
 __device__ __forceinline__ Dig dig_wave_scan(Dig x) {
-    const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const Dig up = dig_shfl_up(x, o);
-        if (lane >= o) dig_add(x, up);
+    for (int i = 0; i < VF_ND; ++i) {
+        uint64_t v = x.d[i];
+        v += dpp64<0x111>(v);
+        v += dpp64<0x112>(v);
+        v += dpp64<0x114>(v);
+        v += dpp64<0x118>(v);
+        v += dpp64<0x142, 0xa>(v);
+        v += dpp64<0x143, 0xc>(v);
+        x.d[i] = v;
     }
     return x;
 }
@@ -516,12 +537,7 @@ __device__ int wg_search(const WRow& r, int a, int len, const Nat& thr, Dig* sh_
 #pragma unroll
             for (int e = 0; e < 4; ++e) dig_add_w(mine, w[e]);
             // inclusive scan over the lanes
-            Dig inc = mine;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const Dig up = dig_shfl_up(inc, o);
-                if (lane >= o) dig_add(inc, up);
-            }
+            Dig inc = dig_wave_scan(mine);
             Dig tot = inc;
             dig_add(tot, base);
             const uint64_t hit = __ballot(nat_gt(nat_of(tot), rem));
@@ -546,7 +562,8 @@ __device__ int wg_search(const WRow& r, int a, int len, const Nat& thr, Dig* sh_
                 // the wave total is lane 63's inclusive prefix
 #pragma unroll
                 for (int k = 0; k < VF_ND; ++k) {
-                    const uint32_t lo = __shfl((uint32_t)inc.d[k], 63, 64), hi = __shfl((uint32_t)(inc.d[k] >> 32), 63, 64);
+                    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)inc.d[k], 63);
+                    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(inc.d[k] >> 32), 63);
                     base.d[k] += ((uint64_t)hi << 32) | lo;
                 }
             }
