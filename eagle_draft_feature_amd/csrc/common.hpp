@@ -53,23 +53,46 @@ __device__ __forceinline__ uint32_t load_coherent_u32(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+// Cross-lane sums in registers (no LDS round trip); the whole wave must be
+// active.  v plus the value of lane l ^ 16 (l ^ 32): a gfx950 permlane swap
+// of v with itself hands every lane its own value and its partner's.
+__device__ __forceinline__ float xor16_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// v moved by one DPP control within each 16-lane row
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+// v plus the value of lane l ^ 1, then of lane l ^ 2 (quad permutations):
+// every lane of a quad ends with the quad's sum
+__device__ __forceinline__ float quad_sum(float v) {
+    v += dpp_f<0xb1>(v);  // quad_perm [1, 0, 3, 2]
+    v += dpp_f<0x4e>(v);  // quad_perm [2, 3, 0, 1]
     return v;
 }
 
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+// Sum over the wave, the butterfly over lane masks 32, 16, 8, 4, 2, 1 (every
+// lane ends with the same bits).  Masks 32 and 16 are permlane swaps, mask 8
+// the row rotation by 8; after those steps a lane's value depends on its
+// index mod 8 only, so the rotations by 4, 2 and 1 reach a lane that holds the
+// same value as lane l ^ 4, l ^ 2, l ^ 1: the adds are those of the butterfly.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = xor32_sum(v);
+    v = xor16_sum(v);
+    v += dpp_f<0x128>(v);  // row_ror:8
+    v += dpp_f<0x124>(v);  // row_ror:4
+    v += dpp_f<0x122>(v);  // row_ror:2
+    v += dpp_f<0x121>(v);  // row_ror:1
     return v;
 }
 
 // Sum over the four 16-lane groups (lanes l, l^16, l^32, l^48 share an MFMA row).
-__device__ __forceinline__ float group4_sum(float v) {
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
-}
+__device__ __forceinline__ float group4_sum(float v) { return xor32_sum(xor16_sum(v)); }
 
 }  // namespace e31

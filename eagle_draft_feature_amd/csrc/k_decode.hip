@@ -153,8 +153,7 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
                     *reinterpret_cast<const uint4*>(hs + shift_src * lds + (tp0 * 32 - seg_k0) + (tid & 3) * 8);
                 float v = bf_lo(x.x) + bf_hi(x.x) + bf_lo(x.y) + bf_hi(x.y) + bf_lo(x.z) + bf_hi(x.z) +
                           bf_lo(x.w) + bf_hi(x.w);
-                v += __shfl_xor(v, 1, 64);
-                v += __shfl_xor(v, 2, 64);
+                v = quad_sum(v);
                 if ((tid & 3) == 0) sh_shift[m] = v * (1.0f / 32.0f);
             }
         }
@@ -519,8 +518,7 @@ __device__ __forceinline__ void one_row_sums(const uint16_t* row, int d, int lan
         const uint4 x = *reinterpret_cast<const uint4*>(row + 8 * (lane & 3));
         float v = ((bf_lo(x.x) + bf_hi(x.x)) + (bf_lo(x.y) + bf_hi(x.y))) +
                   ((bf_lo(x.z) + bf_hi(x.z)) + (bf_lo(x.w) + bf_hi(x.w)));
-        v += __shfl_xor(v, 1, 64);
-        v += __shfl_xor(v, 2, 64);
+        v = quad_sum(v);
         K = v * (1.0f / 32.0f);
     }
     // chunks lane, lane + 64, ... in order; the 8 loads of a batch are

@@ -119,8 +119,7 @@ __device__ __forceinline__ void row_sums_pre(const uint16_t* row, int d, int lan
         const uint4 x = pre.k;
         float v = ((bf_lo(x.x) + bf_hi(x.x)) + (bf_lo(x.y) + bf_hi(x.y))) +
                   ((bf_lo(x.z) + bf_hi(x.z)) + (bf_lo(x.w) + bf_hi(x.w)));
-        v += __shfl_xor(v, 1, 64);
-        v += __shfl_xor(v, 2, 64);
+        v = quad_sum(v);
         K = v * (1.0f / 32.0f);
     }
     float s1 = 0.f, s2 = 0.f;
@@ -682,8 +681,7 @@ __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
                 const uint4 x = *reinterpret_cast<const uint4*>(row + 16 * (lane & 3));
                 float v = ((bf_lo(x.x) + bf_hi(x.x)) + (bf_lo(x.y) + bf_hi(x.y))) +
                           ((bf_lo(x.z) + bf_hi(x.z)) + (bf_lo(x.w) + bf_hi(x.w)));
-                v += __shfl_xor(v, 1, 64);
-                v += __shfl_xor(v, 2, 64);
+                v = quad_sum(v);
                 K = v * (1.0f / 32.0f);
             }
             float s1 = 0.f, s2 = 0.f;
@@ -846,18 +844,6 @@ __device__ __forceinline__ float row_mod_sum(float v) {
     if (MP <= 2) v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false));
     if (MP <= 1) v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false));
     return v;
-}
-
-// v plus the value of the lane 16 (32) apart, in every lane: one gfx950
-// permlane swap of v with itself hands each lane its partner's value, with no
-// LDS round trip (the whole wave must be active)
-__device__ __forceinline__ float xor16_sum(float v) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float xor32_sum(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 template <int NORM, int SB, int R>
