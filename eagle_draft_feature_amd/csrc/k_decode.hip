@@ -510,28 +510,41 @@ __global__ __launch_bounds__(DTHREADS) void decode_kernel(DecodeArgs a) {
 // partials and counter, as in the other decode kernels): the result is
 // bitwise reproducible.
 constexpr int ONE_ROWS_MAX = 16384;  // K rows per chunk (64 KiB of fp32 in LDS)
+constexpr int ONE_XP = 4;            // xn rows per thread whose values are loaded before the W ring
+constexpr int ONE_MAXKC = 72;        // K chunks of a column group, at most (d = 1536 takes 72)
 
-__device__ __forceinline__ void one_row_sums(const uint16_t* row, int d, int lane, bool shift, float& K, float& S1,
-                                             float& S2) {
+// The row's shift piece and first batch (4096 values), loaded by the caller
+// ahead of its other loads (they complete in issue order)
+struct OneRowPre {
+    uint4 k;
+    uint4 x[8];
+};
+__device__ __forceinline__ void one_row_preload(const uint16_t* row, int d, int lane, OneRowPre& pre) {
+    pre.k = *reinterpret_cast<const uint4*>(row + 8 * (lane & 3));
+    const int nchunk = d >> 3;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int c = lane + 64 * q;
+        pre.x[q] = c < nchunk ? *reinterpret_cast<const uint4*>(row + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+__device__ __forceinline__ void one_row_sums(const uint16_t* row, int d, int lane, bool shift, const OneRowPre& pre,
+                                             float& K, float& S1, float& S2) {
     K = 0.f;
     if (shift) {
-        const uint4 x = *reinterpret_cast<const uint4*>(row + 8 * (lane & 3));
+        const uint4 x = pre.k;
         float v = ((bf_lo(x.x) + bf_hi(x.x)) + (bf_lo(x.y) + bf_hi(x.y))) +
                   ((bf_lo(x.z) + bf_hi(x.z)) + (bf_lo(x.w) + bf_hi(x.w)));
         v = quad_sum(v);
         K = v * (1.0f / 32.0f);
     }
     // chunks lane, lane + 64, ... in order; the 8 loads of a batch are
-    // issued before any is used (one round trip per 4096 values)
+    // issued before any is used (one round trip per 4096 values; the first
+    // batch is the preloaded one)
     float s1 = 0.f, s2 = 0.f;
     const int nchunk = d >> 3;
-    for (int c0 = 0; c0 < nchunk; c0 += 512) {
-        uint4 x[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int c = c0 + lane + 64 * q;
-            x[q] = c < nchunk ? *reinterpret_cast<const uint4*>(row + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
-        }
+    auto batch = [&](const uint4 (&x)[8], int c0) __attribute__((always_inline)) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             if (c0 + lane + 64 * q >= nchunk) continue;
@@ -543,6 +556,16 @@ __device__ __forceinline__ void one_row_sums(const uint16_t* row, int d, int lan
                 s2 = fmaf(x0, x0, fmaf(x1, x1, s2));
             }
         }
+    };
+    batch(pre.x, 0);
+    for (int c0 = 512; c0 < nchunk; c0 += 512) {
+        uint4 x[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int c = c0 + lane + 64 * q;
+            x[q] = c < nchunk ? *reinterpret_cast<const uint4*>(row + 8 * c) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        batch(x, c0);
     }
     S1 = wave_sum(s1);
     S2 = wave_sum(s2);
@@ -565,6 +588,32 @@ __global__ __launch_bounds__(512) void decode_one_kernel(DecodeArgs a) {
     const int grp = lin / nkc, kc = lin - grp * nkc;
     const int n0 = 512 * grp, k0 = kc * rows;
 
+    // the token's source row (an invalid index reads row 0; the output is zeros)
+    bool tok_ok;
+    const size_t src0 = (size_t)rv_src(a.rv, 0, tok_ok);
+    // Loads complete in issue order, so the ones waited on first go out
+    // first: the statistics rows (waves 0..2), this chunk's token values and
+    // their gamma and beta (rows tid + 512 j, clamped: a load under a branch
+    // would wait for itself), and the bias; then the W ring.
+    OneRowPre pre;
+    if (NORM != NORM_NONE && wave < 3) one_row_preload(a.h[wave] + src0 * (size_t)rv_ld(a.rv, wave), d, lane, pre);
+    uint16_t xh[ONE_XP], xg[ONE_XP], xb[ONE_XP];
+#pragma unroll
+    for (int j = 0; j < ONE_XP; ++j) {
+        const int k = k0 + min(tid + 512 * j, rows - 1), s = k / d, kk = k - s * d;
+        xh[j] = ((s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2])) + src0 * (size_t)rv_ld(a.rv, s))[kk];
+        xg[j] = xb[j] = 0;
+        if (NORM != NORM_NONE) {
+            const uint16_t* gs = s == 0 ? a.gamma[0] : (s == 1 ? a.gamma[1] : a.gamma[2]);
+            xg[j] = gs ? gs[kk] : (uint16_t)0x3f80;  // bf16 1.0
+            if (NORM == NORM_LN) {
+                const uint16_t* bs = s == 0 ? a.beta[0] : (s == 1 ? a.beta[1] : a.beta[2]);
+                xb[j] = bs ? bs[kk] : (uint16_t)0;
+            }
+        }
+    }
+    const float bias_n = a.bias ? bf_one(a.bias[n0 + tid]) : 0.f;
+
     // this wave's W rows: k0 + wave + 8 i, columns n0 + 8 lane .. + 7
     const uint16_t* __restrict__ wp = a.W + (size_t)(k0 + wave) * d + n0 + 8 * lane;
     const size_t wstep = (size_t)8 * d;
@@ -573,13 +622,10 @@ __global__ __launch_bounds__(512) void decode_one_kernel(DecodeArgs a) {
 #pragma unroll
     for (int p = 0; p < R; ++p) rw[p] = load_w_nt<uint4>(wp + (size_t)p * wstep);
 
-    // the token's source row (an invalid index reads row 0; the output is zeros)
-    bool tok_ok;
-    const size_t src0 = (size_t)rv_src(a.rv, 0, tok_ok);
     // statistics of the three rows (waves 0..2)
     if (NORM != NORM_NONE && wave < 3) {
         float K, S1, S2;
-        one_row_sums(a.h[wave] + src0 * (size_t)rv_ld(a.rv, wave), d, lane, NORM == NORM_LN, K, S1, S2);
+        one_row_sums(a.h[wave] + src0 * (size_t)rv_ld(a.rv, wave), d, lane, NORM == NORM_LN, pre, K, S1, S2);
         if (lane == 0) {
             const float inv_d = 1.0f / (float)d;
             float mu = 0.f, rstd;
@@ -595,8 +641,24 @@ __global__ __launch_bounds__(512) void decode_one_kernel(DecodeArgs a) {
         }
     }
     __syncthreads();
-    // xn of this chunk's rows, in fp32
-    for (int r = tid; r < rows; r += 512) {
+    // xn of this chunk's rows, in fp32: the first ONE_XP rows per thread from
+    // the values loaded up front, any further ones loaded here
+#pragma unroll
+    for (int j = 0; j < ONE_XP; ++j) {
+        const int r = tid + 512 * j;
+        if (r >= rows) break;
+        const int s = (k0 + r) / d;
+        float x = bf_one(xh[j]);
+        if (NORM != NORM_NONE) {
+            x = (x - st[s][0]) * st[s][1] * bf_one(xg[j]);
+            if (NORM == NORM_LN) {
+                const uint16_t* bs = s == 0 ? a.beta[0] : (s == 1 ? a.beta[1] : a.beta[2]);
+                if (bs) x += bf_one(xb[j]);
+            }
+        }
+        xn[r] = x;
+    }
+    for (int r = tid + 512 * ONE_XP; r < rows; r += 512) {
         const int k = k0 + r, s = k / d, kk = k - s * d;
         const uint16_t* hs = (s == 0 ? a.h[0] : (s == 1 ? a.h[1] : a.h[2])) + src0 * (size_t)rv_ld(a.rv, s);
         float x = bf_one(hs[kk]);
@@ -657,18 +719,29 @@ __global__ __launch_bounds__(512) void decode_one_kernel(DecodeArgs a) {
     __syncthreads();
     if (!sh_last) return;
     {
-        // chunks summed in order; each batch of 8 loads is issued before use
+        // chunks summed in order; every chunk's load is issued before any is
+        // used (indexes past nkc re-read the last chunk and are dropped), so
+        // the sum costs one round trip
         const float* gp = a.part + (size_t)grp * nkc * 512 + tid;
         float y = 0.f;
-        for (int c0 = 0; c0 < nkc; c0 += 8) {
-            float v[8];
+        auto sum_chunks = [&](auto nmax) __attribute__((always_inline)) {
+            constexpr int NK = decltype(nmax)::value;
+            float v[NK];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = c0 + q < nkc ? load_coherent(gp + (size_t)(c0 + q) * 512) : 0.f;
+            for (int q = 0; q < NK; ++q) v[q] = load_coherent(gp + (size_t)min(q, nkc - 1) * 512);
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                if (c0 + q < nkc) y += v[q];
-        }
-        if (a.bias) y += bf_one(a.bias[n0 + tid]);
+            for (int q = 0; q < NK; ++q)
+                if (q < nkc) y += v[q];
+        };
+        if (nkc <= 16)
+            sum_chunks(std::integral_constant<int, 16>());
+        else if (nkc <= 32)
+            sum_chunks(std::integral_constant<int, 32>());
+        else if (nkc <= 48)
+            sum_chunks(std::integral_constant<int, 48>());
+        else
+            sum_chunks(std::integral_constant<int, ONE_MAXKC>());
+        if (a.bias) y += bias_n;
         a.out[n0 + tid] = tok_ok ? (uint16_t)(pack_bf2(y, 0.f) & 0xffffu) : (uint16_t)0;
     }
     if (tid == 0) __hip_atomic_store(a.counters + grp, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -684,6 +757,7 @@ DecodePlan plan_decode(int M, int d, int norm) {
         for (int nkc = 1; nkc <= 256 && ngroups * nkc <= 256; ++nkc) {
             if ((3 * d) % (nkc * 64) != 0) continue;  // rows per chunk: 8 waves x a multiple of 8 steps
             if (3 * d / nkc > ONE_ROWS_MAX) continue;
+            if (nkc > ONE_MAXKC) break;
             best = nkc;
         }
         if (best) {
@@ -744,7 +818,7 @@ static hipError_t launch_one(const DecodeArgs& a, const DecodePlan& p, hipStream
 hipError_t launch_decode(const DecodeArgs& a, int norm, const DecodePlan& p, hipStream_t st) {
     if (p.one) {
         if (a.M != 1 || a.nb != p.nb || a.kps != p.kps || a.d != 512 * p.nb || (3 * a.d) % (p.kps * 64) ||
-            3 * a.d / p.kps > ONE_ROWS_MAX)
+            3 * a.d / p.kps > ONE_ROWS_MAX || p.kps > ONE_MAXKC)
             return hipErrorInvalidValue;
         if (norm == NORM_LN) return launch_one<NORM_LN>(a, p, st);
         if (norm == NORM_RMS) return launch_one<NORM_RMS>(a, p, st);
