@@ -622,7 +622,7 @@ constexpr int WH_WAVES = 8;
 template <int NORM, int R, int MM>
 __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
     __shared__ __attribute__((aligned(16))) char la[MM * (6 * 4096 + 64)];
-    __shared__ f32x4 red[WH_WAVES][3][64];
+    __shared__ f32x4 red[WH_WAVES][3][16];  // the tiles' first row group (rows 0..3 hold the tokens)
     __shared__ float sst[3 * MM][3];
     const int M = a.M, d = a.d;
     const int T3 = d >> 5, JS = T3 / WH_WAVES;  // k-steps per state and wave
@@ -665,6 +665,13 @@ __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
 #pragma unroll
     for (int p = 0; p < R; ++p) rw[p] = __builtin_nontemporal_load(&wp[(size_t)p * WSTEP]);
     __builtin_amdgcn_sched_barrier(0);
+    // c and u of this lane's column, needed at the end only: behind the ring
+    const int n = 16 * grp + cb;
+    const float cn = a.c[n];
+    float un[3] = {0.f, 0.f, 0.f};
+    if (NORM == NORM_LN)
+#pragma unroll
+        for (int q = 0; q < 3; ++q) un[q] = a.u[(size_t)q * d + n];
 
 #pragma unroll
     for (int i = 0; i < ACH; ++i)
@@ -738,41 +745,59 @@ __global__ __launch_bounds__(64 * WH_WAVES) void gemv_whole_kernel(GemvArgs a) {
             }
         }
     };
+    // each state's tile rows 0..3 (lanes 0..15) to LDS as soon as it is done
     run_state(acc[0], 0, false);
+    if (g == 0) red[wave][0][lane] = acc[0];
     run_state(acc[1], JS, false);
+    if (g == 0) red[wave][1][lane] = acc[1];
     run_state(acc[2], 2 * JS, true);
-
-#pragma unroll
-    for (int q = 0; q < 3; ++q) red[wave][q][lane] = acc[q];
+    if (g == 0) red[wave][2][lane] = acc[2];
     __syncthreads();
     if (wave != 0) return;
-    f32x4 P[3];
+
+    // wave 0, every LDS read issued before any is used: lane (g, cb) reads
+    // waves 2 g, 2 g + 1 of the rows e < MM (a fixed tree over the waves
+    // with the cross-row sums below); lane MM q + m turns the sums of
+    // (state q, token m) into (mu, rstd) (lanes past 3 MM take state 2's, unused)
+    static_assert(WH_WAVES == 8, "the tree takes two waves per 16-lane row");
+    float tv[3][2][MM];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-        P[q] = red[0][q][lane];
+    for (int q = 0; q < 3; ++q)
 #pragma unroll
-        for (int w = 1; w < WH_WAVES; ++w) P[q] += red[w][q][lane];
+        for (int w = 0; w < 2; ++w)
+#pragma unroll
+            for (int e = 0; e < MM; ++e) tv[q][w][e] = reinterpret_cast<const float*>(&red[2 * g + w][q][cb])[e];
+    float stl[3] = {0.f, 0.f, 0.f};
+    if (NORM != NORM_NONE) {
+        const int it = min(lane / MM, 2) * M + min(lane % MM, M - 1);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) stl[k] = sst[it][k];
     }
-    // lane (g, cb): rows 4 g + e, column 16 grp + cb
-    const int n = 16 * grp + cb;
-    const float cn = a.c[n];
+    __builtin_amdgcn_sched_barrier(0);
+    float mu = 0.f, rs = 1.f;
+    if (NORM != NORM_NONE) row_norm<NORM>(stl, d, a.eps, mu, rs);
+    float P[3][MM];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int m = 4 * g + e;
-        if (m >= M) continue;
+    for (int q = 0; q < 3; ++q)
+#pragma unroll
+        for (int e = 0; e < MM; ++e) P[q][e] = xor32_sum(xor16_sum(tv[q][0][e] + tv[q][1][e]));
+    // lane (0, cb): rows e, column n; (mu, rstd) of a row read from its lane
+#pragma unroll
+    for (int e = 0; e < MM; ++e) {
         float y = cn;
 #pragma unroll
         for (int q = 0; q < 3; ++q) {
-            float mu = 0.f, r = 1.f;
+            float muq = 0.f, rq = 1.f;
             if (NORM != NORM_NONE) {
-                const float stt[3] = {sst[q * M + m][0], sst[q * M + m][1], sst[q * M + m][2]};
-                row_norm<NORM>(stt, d, a.eps, mu, r);
+                muq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mu), MM * q + e));
+                rq = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rs), MM * q + e));
             }
             float pv = P[q][e];
-            if (NORM == NORM_LN) pv -= mu * a.u[(size_t)q * d + n];
-            y += (NORM == NORM_NONE) ? pv : r * pv;
+            if (NORM == NORM_LN) pv -= muq * un[q];
+            y += (NORM == NORM_NONE) ? pv : rq * pv;
         }
-        a.out[(size_t)m * (size_t)a.rv.ld_out + n] = rv_ok(wr, m) ? (uint16_t)(pack_bf2(y, 0.f) & 0xffffu) : (uint16_t)0;
+        if (g == 0 && e < M)
+            a.out[(size_t)e * (size_t)a.rv.ld_out + n] = rv_ok(wr, e) ? (uint16_t)(pack_bf2(y, 0.f) & 0xffffu) : (uint16_t)0;
     }
 }
 
