@@ -891,11 +891,20 @@ __global__ __launch_bounds__(64 * PK_WAVES) void gemv_pack_kernel(GemvArgs a) {
     const int jl = cb / MP, rl = cb % MP;
     const bool rvalid = rl < M;
     const size_t brow = (size_t)rv_lane_src(a.rv, wr, min(rl, M - 1));
-    // state s's block of the wave's local steps [t, t + SB): bs + 512 t
-    const char* const b0 = reinterpret_cast<const char*>(a.h[0] + brow * (size_t)a.rv.ld[0]) + 16 * g + 64 * (wave + 8 * jl);
-    const char* const b1 = reinterpret_cast<const char*>(a.h[1] + brow * (size_t)a.rv.ld[1]) + 16 * g + 64 * (wave + 8 * jl);
-    const char* const b2 = reinterpret_cast<const char*>(a.h[2] + brow * (size_t)a.rv.ld[2]) + 16 * g + 64 * (wave + 8 * jl);
-    constexpr int BSTEP = 64 * PK_WAVES;  // bytes between a wave's steps
+    // Wave w takes runs of RL consecutive k-steps of each state: its local
+    // step l is the state's k-step RL w + 8 RL (l / RL) + l % RL.  With RL =
+    // SB a packed block holds SB consecutive k-steps, SB x 64 contiguous bytes
+    // of each token row; in the wave-strided order (RL = 1) its pieces are
+    // 64 bytes each, 512 bytes apart.  Runs measured faster from four k-steps
+    // per block on (d = 8192, one token: 60.5 against 63.6 us) and slower at
+    // two (six tokens: eight rows of 128 bytes, 21.3 against 20.3 us).
+    // State s's block of the local steps [t, t + SB): bs + 512 t.
+    constexpr int RL = SB >= 4 ? SB : 1;
+    const int boff = 64 * (RL * wave + (RL == 1 ? PK_WAVES * jl : jl));
+    const char* const b0 = reinterpret_cast<const char*>(a.h[0] + brow * (size_t)a.rv.ld[0]) + 16 * g + boff;
+    const char* const b1 = reinterpret_cast<const char*>(a.h[1] + brow * (size_t)a.rv.ld[1]) + 16 * g + boff;
+    const char* const b2 = reinterpret_cast<const char*>(a.h[2] + brow * (size_t)a.rv.ld[2]) + 16 * g + boff;
+    constexpr int BSTEP = 64 * PK_WAVES;  // bytes per local step between blocks
 
     // shift rows (LayerNorm): lane (g, cb) holds the values 8 g .. of each
     // state's first k-step of its own token row; c and u of this lane's column
@@ -917,12 +926,13 @@ __global__ __launch_bounds__(64 * PK_WAVES) void gemv_pack_kernel(GemvArgs a) {
     u32x4 ab[NBB];
 #pragma unroll
     for (int bb = 0; bb < NBB; ++bb) ab[bb] = *reinterpret_cast<const u32x4*>(b0 + bb * SB * BSTEP);
-    const u32x4* __restrict__ wp = reinterpret_cast<const u32x4*>(a.wp) + ((size_t)grp * 3 * T3 + wave) * 64 + lane;
-    constexpr int WSTEP = PK_WAVES * 64;  // uint4 between a wave's steps
+    // the W' tile of local step l (over the three states in turn), in uint4
+    const u32x4* __restrict__ wp = reinterpret_cast<const u32x4*>(a.wp) + ((size_t)grp * 3 * T3 + RL * wave) * 64 + lane;
+    auto woff = [](int l) __attribute__((always_inline)) { return (size_t)(PK_WAVES * RL * (l / RL) + l % RL) * 64; };
     u32x4 rw[R];
 #pragma unroll
     for (int p = 0; p < R; ++p) {
-        rw[p] = __builtin_nontemporal_load(&wp[(size_t)p * WSTEP]);
+        rw[p] = __builtin_nontemporal_load(&wp[woff(p)]);
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -983,7 +993,7 @@ __global__ __launch_bounds__(64 * PK_WAVES) void gemv_pack_kernel(GemvArgs a) {
                 const int p = bb * SB + j;
                 ac = mfma16x16x32(j == 0 ? ab[bb] : fr[j], rw[p % R], ac);
                 if (refill == 1 || (refill == 2 && p + R < U))
-                    rw[p % R] = __builtin_nontemporal_load(&wp[(size_t)(j0 + i + p + R) * WSTEP]);
+                    rw[p % R] = __builtin_nontemporal_load(&wp[woff(j0 + i + p + R)]);
                 if (j == 0 && refill == 1) ab[bb] = *reinterpret_cast<const u32x4*>(anext + (nexti + bb * SB) * BSTEP);
                 __builtin_amdgcn_sched_barrier(0);
             }
