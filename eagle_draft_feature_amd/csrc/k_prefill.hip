@@ -450,7 +450,7 @@ __global__ __launch_bounds__(PTH, 1) void prefill_kernel(PrefillArgs a, int TM, 
 // kernel.  y = sum_s rstd_s (sum over the chunks of state s, in their order,
 // - mu_s u_s) + c, stored through the same quad exchange.  It runs after the
 // main kernel on the stream, so plain loads see the partials.
-template <int NORM>
+template <int NORM, int KPS>
 __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillArgs a, int TM, int TN) {
     const int lane = threadIdx.x & 63, g = lane >> 4, cb = lane & 15;
     const int fg = blockIdx.x * 4 + (threadIdx.x >> 6);  // 256 fragment groups per tile
@@ -463,40 +463,68 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(PrefillArgs a, int 
     const int row0 = mt * PBM + wm * 128 + 16 * i + 4 * g;
     if (mt * PBM + wm * 128 + 16 * i >= M) return;  // whole wave: rows the main kernel did not store
     const int col = nt * PBN + wn * 128 + 16 * j + cb;
-    const int splits = a.splits, kps = splits / 3;
+    const int splits = a.splits;  // 3 KPS
     const f32x4* part = reinterpret_cast<const f32x4*>(a.part) + (size_t)tile * splits * PTH * 64 + (size_t)(ij * 4 + w) * 64 + lane;
+    // Every load goes out before any value is used (a value tested inside
+    // the branch of its own load waits for all loads in flight): the row
+    // indices, the rows' statistics, c and u, then exactly KPS partials per
+    // state; the empty asm statements keep the compiler from sinking a load
+    // into the branch of a later use.  Without an index list the index load
+    // reads c (a device array here) and is dropped; columns past d read
+    // column d - 1 and are not stored.
+    const bool has_idx = a.rv.idx != nullptr;
+    const int* ip = has_idx ? a.rv.idx : reinterpret_cast<const int*>(a.c);
+    int raw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) raw[e] = ip[has_idx ? min(row0 + e, M - 1) : 0];
+    float mu_r[3][4], rs_r[3][4];
+#pragma unroll
+    for (int ss = 0; ss < 3; ++ss)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int m = min(row0 + e, M - 1);
+            mu_r[ss][e] = NORM == NORM_LN ? a.mu[(size_t)ss * M + m] : 0.f;
+            rs_r[ss][e] = NORM != NORM_NONE ? a.rstd[(size_t)ss * M + m] : 1.f;
+        }
+    const bool colok = col < d;
+    const int colc = min(col, d - 1);
+    const float cl = a.c[colc];
+    float ul[3] = {0.f, 0.f, 0.f};
+    if (NORM == NORM_LN)
+#pragma unroll
+        for (int ss = 0; ss < 3; ++ss) ul[ss] = a.u[(size_t)ss * d + colc];
+    f32x4 v[3][KPS];
+#pragma unroll
+    for (int ss = 0; ss < 3; ++ss)
+#pragma unroll
+        for (int ch = 0; ch < KPS; ++ch) v[ss][ch] = part[(size_t)(ss * KPS + ch) * PTH * 64];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) asm volatile("" : "+v"(raw[e]));
     f32x4 ps[3];
 #pragma unroll
     for (int ss = 0; ss < 3; ++ss) {
-        f32x4 v[8];
+        ps[ss] = v[ss][0];
 #pragma unroll
-        for (int ch = 0; ch < 8; ++ch)
-            v[ch] = ch < kps ? part[(size_t)(ss * kps + ch) * PTH * 64] : f32x4{0.f, 0.f, 0.f, 0.f};
-        ps[ss] = v[0];
-#pragma unroll
-        for (int ch = 1; ch < 8; ++ch)
-            if (ch < kps) ps[ss] += v[ch];
+        for (int ch = 1; ch < KPS; ++ch) ps[ss] += v[ss][ch];
     }
-    const bool colok = col < d;
-    const float cn = colok ? a.c[col] : 0.f;
+    const float cn = colok ? cl : 0.f;
     float uc[3] = {0.f, 0.f, 0.f};
     if (NORM == NORM_LN && colok)
 #pragma unroll
-        for (int ss = 0; ss < 3; ++ss) uc[ss] = a.u[(size_t)ss * d + col];
+        for (int ss = 0; ss < 3; ++ss) uc[ss] = ul[ss];
     float y[4];
     uint32_t okbits = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const int m = min(row0 + e, M - 1);
-        bool ok;
-        (void)rv_src(a.rv, m, ok);
+        const int r = has_idx ? raw[e] : min(row0 + e, M - 1);  // a dense call's row is its own
+        const bool ok = r >= 0 && r < a.rv.n_src;
         okbits |= ok ? (1u << e) : 0u;
         float acc = cn;
 #pragma unroll
         for (int ss = 0; ss < 3; ++ss) {
             float pv = ps[ss][e];
-            if (NORM == NORM_LN) pv -= a.mu[(size_t)ss * M + m] * uc[ss];
-            acc += NORM == NORM_NONE ? pv : a.rstd[(size_t)ss * M + m] * pv;
+            if (NORM == NORM_LN) pv -= mu_r[ss][e] * uc[ss];
+            acc += NORM == NORM_NONE ? pv : rs_r[ss][e] * pv;
         }
         y[e] = acc;
     }
@@ -543,8 +571,20 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, const PrefillPlan& p, h
     if (SPLIT) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        // 256 fragment groups per tile, 4 per workgroup
-        prefill_reduce_kernel<NORM><<<p.tiles_m * p.tiles_n * 64, 256, 0, st>>>(a, p.tiles_m, p.tiles_n);
+        // 256 fragment groups per tile, 4 per workgroup; the chunks per state
+        // (parts per state in the four-chunk mode) are a template argument
+        const int rg = p.tiles_m * p.tiles_n * 64;
+        switch (a.splits / 3) {
+            case 1: prefill_reduce_kernel<NORM, 1><<<rg, 256, 0, st>>>(a, p.tiles_m, p.tiles_n); break;
+            case 2: prefill_reduce_kernel<NORM, 2><<<rg, 256, 0, st>>>(a, p.tiles_m, p.tiles_n); break;
+            case 3: prefill_reduce_kernel<NORM, 3><<<rg, 256, 0, st>>>(a, p.tiles_m, p.tiles_n); break;
+            case 4: prefill_reduce_kernel<NORM, 4><<<rg, 256, 0, st>>>(a, p.tiles_m, p.tiles_n); break;
+            case 5: prefill_reduce_kernel<NORM, 5><<<rg, 256, 0, st>>>(a, p.tiles_m, p.tiles_n); break;
+            case 6: prefill_reduce_kernel<NORM, 6><<<rg, 256, 0, st>>>(a, p.tiles_m, p.tiles_n); break;
+            case 7: prefill_reduce_kernel<NORM, 7><<<rg, 256, 0, st>>>(a, p.tiles_m, p.tiles_n); break;
+            case 8: prefill_reduce_kernel<NORM, 8><<<rg, 256, 0, st>>>(a, p.tiles_m, p.tiles_n); break;
+            default: return hipErrorInvalidValue;
+        }
     }
     return hipGetLastError();
 }
